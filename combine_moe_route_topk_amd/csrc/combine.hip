@@ -1,0 +1,170 @@
+// Combine: gather each token's k value rows, dequantize, gate-weighted sum.
+//
+// [XDS 合设 A2A, COMBINE procedure (result[token] += value * gate weight);
+//  CMI EP320 FusedCombine (all k contributions present, dequantize, weight by
+//  the gate)]
+//
+// One wavefront per token.  The k row gathers of an element group are issued
+// together (k x 16 B per lane in flight), then summed in fp32 in ascending
+// route order with separate multiply and add (no FMA contraction), so the
+// result is the same bits as the plain loop on the CPU.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <bool Q8, bool OUT_BF16, int KMAX>
+__global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict__ src,
+                                                      const int32_t *__restrict__ row,
+                                                      const float *__restrict__ topk_w, int T,
+                                                      int H, int k, int64_t row_bytes,
+                                                      void *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int64_t my_row = -1;
+  float my_w = 0.0f, my_s = 0.0f;
+  if (lane < k) {
+    my_row = row[t * k + lane];
+    my_w = topk_w[t * k + lane];
+    if (Q8 && my_row >= 0) my_s = *(const float *)(src + my_row * row_bytes + H);
+  }
+  const uint8_t *base[KMAX];
+  float w[KMAX], sc[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int64_t r = __shfl(my_row, j, 64);
+    w[j] = __shfl(my_w, j, 64);
+    sc[j] = __shfl(my_s, j, 64);
+    base[j] = (j < k && r >= 0) ? src + r * row_bytes : nullptr;
+  }
+  constexpr int EPL = Q8 ? 16 : 8;  // elements per lane per 16-byte load
+  const int iters = (H + 64 * EPL - 1) / (64 * EPL);
+  for (int i = 0; i < iters; ++i) {
+    const int e0 = (i * 64 + lane) * EPL;
+    if (e0 >= H) break;
+    uint4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (base[j]) v[j] = *(const uint4 *)(base[j] + (Q8 ? e0 : 2 * e0));
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (!base[j]) continue;
+      const uint32_t *wd = (const uint32_t *)&v[j];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x;
+        if (Q8) {
+          const int8_t q = (int8_t)((wd[e >> 2] >> (8 * (e & 3))) & 0xffu);
+          x = (float)q * sc[j];
+        } else {
+          x = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        }
+        const float prod = w[j] * x;
+        acc[e] = acc[e] + prod;
+      }
+    }
+    if (OUT_BF16) {
+      uint32_t pk[EPL / 2];
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e)
+        pk[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+      uint4 *dst = (uint4 *)((uint16_t *)out + t * H + e0);
+#pragma unroll
+      for (int q = 0; q < EPL / 8; ++q) dst[q] = make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+    } else {
+      float4 *dst = (float4 *)((float *)out + t * H + e0);
+#pragma unroll
+      for (int q = 0; q < EPL / 4; ++q)
+        dst[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    }
+  }
+}
+
+template <int KMAX>
+void launch_combine(bool q8, bool obf, dim3 grid, hipStream_t s, const uint8_t *src,
+                    const int32_t *row, const float *w, const moe_geom_t &g, int64_t rb,
+                    void *out) {
+#define MOE_COMBINE(Q, O)                                                                     \
+  hipLaunchKernelGGL((combine_kernel<Q, O, KMAX>), grid, dim3(256), 0, s, src, row, w, g.T, g.H, \
+                     g.k, rb, out)
+  if (q8 && obf) MOE_COMBINE(true, true);
+  else if (q8) MOE_COMBINE(true, false);
+  else if (obf) MOE_COMBINE(false, true);
+  else MOE_COMBINE(false, false);
+#undef MOE_COMBINE
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *row,
+                           const float *topk_w, const moe_geom_t *g, moe_dtype_t out_dtype,
+                           void *out, void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (g->T > 0 && (!src || !row || !topk_w || !out)) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_RET_Q8_FROM_DISPATCH && mode != MOE_RET_BF16) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if (g->T == 0) return MOE_OK;
+  const bool q8 = mode == MOE_RET_Q8_FROM_DISPATCH;
+  const int64_t rb = q8 ? msg_bytes_of(*g) : (int64_t)g->H * 2;
+  const dim3 grid((unsigned)((g->T + 3) / 4));
+  hipStream_t s = (hipStream_t)stream;
+  const bool obf = out_dtype == MOE_DTYPE_BF16;
+  const uint8_t *sp = (const uint8_t *)src;
+  if (g->k <= 2)
+    launch_combine<2>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+  else if (g->k <= 4)
+    launch_combine<4>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+  else if (g->k <= 8)
+    launch_combine<8>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+  else
+    launch_combine<16>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+  return launch_status();
+}
+
+// ------------------------------------------------------- E2A second hop ---
+namespace moe {
+namespace {
+// One wavefront per route: rows of slots on partitions >= relays are staged
+// after the T*k return rows, and the combine is pointed at the staged copy.
+__global__ __launch_bounds__(256) void relay_returns_kernel(
+    uint16_t *__restrict__ ret, const int32_t *__restrict__ phys,
+    const int32_t *__restrict__ slot_partition, const int32_t *__restrict__ ret_row,
+    int64_t n_routes, int P, int H, int relays, int32_t *__restrict__ comb_row) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gi >= n_routes) return;
+  const int32_t rr = ret_row[gi];
+  const int p = phys[gi];
+  const bool relayed = rr >= 0 && p >= 0 && p < P && slot_partition[p] >= relays;
+  if (lane == 0) comb_row[gi] = relayed ? (int32_t)(n_routes + rr) : rr;
+  if (!relayed) return;
+  const uint4 *src = (const uint4 *)(ret + (int64_t)rr * H);
+  uint4 *dst = (uint4 *)(ret + (n_routes + rr) * H);
+  for (int i = lane; i < H / 8; i += 64) dst[i] = src[i];
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_relay_returns(uint16_t *ret, const int32_t *phys_ids,
+                                 const int32_t *slot_partition, const int32_t *ret_row,
+                                 const moe_geom_t *g, int32_t *comb_row, void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (!ret || !phys_ids || !slot_partition || !ret_row || !comb_row) return MOE_ERR_INVALID_ARG;
+  if (g->relays <= 0 || !aligned16(ret)) return MOE_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)g->T * g->k;
+  if (n == 0) return MOE_OK;
+  hipLaunchKernelGGL(relay_returns_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)stream, ret, phys_ids, slot_partition, ret_row, n, g->P, g->H,
+                     g->relays, comb_row);
+  return launch_status();
+}

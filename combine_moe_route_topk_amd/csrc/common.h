@@ -1,0 +1,77 @@
+// Internal helpers of the HIP library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_route_topk.h"
+
+namespace moe {
+
+// ----------------------------------------------------------- host side ---
+
+inline int64_t msg_bytes_of(const moe_geom_t &g) {
+  return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 15) / 16) * 16;
+}
+inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
+
+// Routes per dispatch chunk: chunks never straddle a source partition.
+constexpr int kChunkRoutes = 256;
+inline int chunk_tokens(const moe_geom_t &g) {
+  int ct = kChunkRoutes / g.k;
+  ct = ct < g.LB ? ct : g.LB;
+  return ct > 0 ? ct : 1;
+}
+inline int64_t chunks_per_source(const moe_geom_t &g) {
+  int ct = chunk_tokens(g);
+  return ((int64_t)g.LB + ct - 1) / ct;
+}
+
+int validate_geom(const moe_geom_t *g);
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+inline int launch_status() { return hip_status(hipGetLastError()); }
+
+// Byte layout of the dispatch scratch (all offsets 256-aligned).
+struct DispatchScratch {
+  int64_t status;       // int32 device status word
+  int64_t hist_d;       // int32 [D][NC+1]  per-chunk route counts per destination partition
+  int64_t hist_p;       // int32 [P][NC+1]  per-chunk route counts per slot
+  int64_t route_rank;   // int32 [T*k]    (rank in chunk for d) | (rank in chunk for p) << 16
+  int64_t slot_local;   // int32 [P]
+  int64_t total;
+};
+DispatchScratch dispatch_scratch_layout(const moe_geom_t &g);
+
+// Byte layout of the expert-FFN scratch.
+struct FfnScratch {
+  int64_t tiles;     // int32 [P + 1]: exclusive prefix of per-slot m-tile counts, then the total
+  int64_t pmax;      // fp32 [T*k][I/64]  max |h| of each row over each gate-up n-tile
+  int64_t h;         // fp32 [T*k][I]
+  int64_t hq;        // int8 [T*k][I]
+  int64_t hs;        // fp32 [T*k]
+  int64_t total;
+};
+FfnScratch ffn_scratch_layout(const moe_geom_t &g, int32_t I);
+
+// ---------------------------------------------------------- device side ---
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+// round to nearest even (finite inputs; NaN is kept a quiet NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,475 @@
+// INT8 dispatch: slot allocation (count phase) + token-wise quantization fused
+// into the scatter of k message copies into static per-partition regions.
+//
+// [XDS 合设 A2A, P039-P040 and Fig. 7: histogram routes per receiver, write
+//  {count, offset} metadata, wait for every sender's metadata, prefix-sum the
+//  received counts, move the data; CMI EP320 FusedDispatch: quantize BF16 to
+//  INT8 + scale early and write message + source info into the target's
+//  static buffer; XDS 解耦 A2A P045 / Fig. 8: two-hop trampoline.]
+//
+// One GPU plays every partition, so the pages' "broadcast counts, then wait
+// for all ranks" barrier becomes the boundary between kernels:
+//   1. count    one block per chunk of <= 256 routes (never straddling a source
+//               partition): stable in-chunk ranks of each route among the
+//               routes with the same destination partition d and the same slot
+//               p, by wavefront ballot multisplit (match masks from one ballot
+//               per key bit, rank = popcount below the lane) plus per-wave
+//               counts in LDS; writes per-chunk histograms over d and over p.
+//   2. scan     one block per d and per p: exclusive prefix of the chunk
+//               histograms in (source, chunk) order.  For d this single prefix
+//               is both the receive layout offset of source s (its value at
+//               s's first chunk) and, relative to it, the chunk's base row in
+//               region (d, s).
+//   3. finalize slot_count / slot_offset / slot_local; clears the status word.
+//   4. scatter  one wavefront per token: amax, scale, IEEE divide + RNE to
+//               int8, 16-byte stores of the k message rows and trailers.
+//   5. relay    (two-hop only) second hop: relay region rows -> final region.
+// No atomics decide any order: every row index is a deterministic function of
+// the routes, so the layout is bit-identical run to run.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// lanes of the wavefront holding the same key (0 for invalid lanes)
+__device__ __forceinline__ uint64_t match_any(int key, int nbits, bool valid) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    m &= bit ? ones : ~ones;
+  }
+  return valid ? m : 0ull;
+}
+
+__device__ __forceinline__ int bits_for(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+// ---------------------------------------------------------------- count ---
+__global__ __launch_bounds__(256) void dispatch_count_kernel(
+    const int32_t *__restrict__ phys, const int32_t *__restrict__ slot_partition, int T, int k,
+    int P, int D, int LB, int ct, int cps, int nc, int32_t *__restrict__ hist_d,
+    int32_t *__restrict__ hist_p, int32_t *__restrict__ route_rank) {
+  extern __shared__ int32_t lds[];
+  int32_t *wd = lds;              // [4][D]
+  int32_t *wp = lds + 4 * D;      // [4][P]
+  const int c = blockIdx.x;
+  const int s = c / cps, ci = c % cps;
+  const int64_t t0 = (int64_t)s * LB + (int64_t)ci * ct;
+  const int64_t t1 = min(t0 + ct, (int64_t)(s + 1) * LB);
+  const int n = (int)(t1 - t0) * k;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < 4 * (D + P); i += 256) lds[i] = 0;
+  __syncthreads();
+
+  const int64_t gi = t0 * k + tid;
+  int p = -1, d = -1, bad = 0;
+  if (tid < n) {
+    p = phys[gi];
+    if (p < 0 || p >= P) {
+      bad = -1;
+    } else {
+      d = slot_partition[p];
+      if (d < 0 || d >= D) bad = -2;
+    }
+  }
+  const bool valid = tid < n && bad == 0;
+  const uint64_t lt = lanemask_lt();
+  const uint64_t md = match_any(d, bits_for(D), valid);
+  const uint64_t mp = match_any(p, bits_for(P), valid);
+  const int rd = __popcll(md & lt), rp = __popcll(mp & lt);
+  if (valid && rd == 0) wd[wave * D + d] = __popcll(md);
+  if (valid && rp == 0) wp[wave * P + p] = __popcll(mp);
+  __syncthreads();
+  if (tid < n) {
+    if (valid) {
+      int bd = rd, bp = rp;
+      for (int w = 0; w < wave; ++w) {
+        bd += wd[w * D + d];
+        bp += wp[w * P + p];
+      }
+      route_rank[gi] = bd | (bp << 16);
+    } else {
+      route_rank[gi] = bad;
+    }
+  }
+  for (int i = tid; i < D; i += 256)
+    hist_d[(int64_t)i * (nc + 1) + c] = wd[i] + wd[D + i] + wd[2 * D + i] + wd[3 * D + i];
+  for (int i = tid; i < P; i += 256)
+    hist_p[(int64_t)i * (nc + 1) + c] = wp[i] + wp[P + i] + wp[2 * P + i] + wp[3 * P + i];
+}
+
+// ----------------------------------------------------------------- scan ---
+// Block b < D scans hist_d row b, block D + p scans hist_p row p: in place,
+// exclusive over the nc chunks, total in column nc.
+__device__ __forceinline__ int block_incl_scan_256(int v, int *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += sh[w];
+  __syncthreads();
+  return v + add;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t *__restrict__ hist_d,
+                                                            int32_t *__restrict__ hist_p, int D,
+                                                            int nc) {
+  __shared__ int sh[4];
+  __shared__ int carry_sh;
+  const bool is_d = blockIdx.x < (unsigned)D;
+  const int row = is_d ? blockIdx.x : blockIdx.x - D;
+  int32_t *h = (is_d ? hist_d : hist_p) + (int64_t)row * (nc + 1);
+  int carry = 0;
+  for (int base = 0; base < nc; base += 256) {
+    const int c = base + threadIdx.x;
+    const int v = c < nc ? h[c] : 0;
+    const int incl = block_incl_scan_256(v, sh);
+    if (c < nc) h[c] = carry + incl - v;
+    if (threadIdx.x == 255) carry_sh = incl;
+    __syncthreads();
+    carry += carry_sh;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) h[nc] = carry;
+}
+
+// -------------------------------------------------------------- finalize ---
+// Block 0: slot_count / slot_offset (P <= 1024) / slot_local, clears the status
+// word.  Blocks 1..: meta[d][s] = {event, prefix at s's first chunk, count}.
+__global__ __launch_bounds__(1024) void dispatch_finalize_kernel(
+    const int32_t *__restrict__ hist_d, const int32_t *__restrict__ hist_p,
+    const int32_t *__restrict__ slot_partition, int D, int P, int S, int cps, int nc,
+    uint32_t event_id, moe_meta_t *__restrict__ meta, int32_t *__restrict__ slot_count,
+    int32_t *__restrict__ slot_offset, int32_t *__restrict__ slot_local,
+    int32_t *__restrict__ status) {
+  if (blockIdx.x > 0) {
+    const int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x;
+    if (i >= (int64_t)D * S) return;
+    const int d = (int)(i / S), s = (int)(i % S);
+    const int32_t *h = hist_d + (int64_t)d * (nc + 1);
+    const int a = h[s * cps], b = h[(s + 1) * cps];  // (s + 1) * cps <= nc: column nc is the total
+    moe_meta_t m;
+    m.event_id = event_id;
+    m.offset = a;
+    m.count = b - a;
+    m.reserved = 0;
+    meta[i] = m;
+    return;
+  }
+  __shared__ int sh[16];
+  __shared__ int part[MOE_MAX_P];
+  const int p = threadIdx.x, lane = p & 63, wave = p >> 6;
+  if (p < P) part[p] = slot_partition[p];
+  const int v = p < P ? hist_p[(int64_t)p * (nc + 1) + nc] : 0;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += sh[w];
+  if (p < P) {
+    slot_count[p] = v;
+    slot_offset[p] = incl - v;
+    if (p == P - 1) slot_offset[P] = incl;
+    const int d = part[p];  // part[] is complete: the scan above passed a barrier
+    int nloc = 0;
+    for (int q = 0; q < p; ++q) nloc += part[q] == d;
+    slot_local[p] = nloc;
+  }
+  if (p == 0) *status = 0;
+}
+
+// -------------------------------------------------------------- scatter ---
+// One wavefront per token.  Lane l, iteration i covers elements
+// [(i*64 + l)*16, +16) of the row: 32 B (bf16) or 64 B (fp32) loads and one
+// 16-byte int8 store per message copy.
+template <int NIT, bool BF16>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const void *__restrict__ x, const int32_t *__restrict__ phys,
+    const int32_t *__restrict__ slot_partition, const int32_t *__restrict__ slot_local,
+    const int32_t *__restrict__ hist_d, const int32_t *__restrict__ hist_p,
+    const int32_t *__restrict__ route_rank, const int32_t *__restrict__ slot_offset, int T,
+    int H, int k, int S, int LB, int ct, int cps, int nc, int64_t cap, int64_t msg, int relays,
+    uint32_t event_id, uint8_t *__restrict__ disp_buf, uint8_t *__restrict__ relay_buf,
+    int32_t *__restrict__ slot_rows, int32_t *__restrict__ disp_row,
+    int32_t *__restrict__ ret_row, int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int s = (int)(t / LB), b = (int)(t % LB);
+  const int c = s * cps + b / ct;
+
+  // ---- per-route row indices (lanes 0..k-1) ----
+  int64_t drow = -1;
+  int dpart = 0;
+  uint32_t tail_w = 0;
+  if (lane < k) {
+    const int64_t gi = t * k + lane;
+    const int rr = route_rank[gi];
+    int32_t out_d = -1, out_r = -1;
+    if (rr < 0) {
+      atomicOr(status, rr == -1 ? MOE_DEVICE_BAD_ROUTE : MOE_DEVICE_BAD_PARTITION);
+    } else {
+      const int p = phys[gi];
+      const int d = slot_partition[p];
+      const int32_t *hd = hist_d + (int64_t)d * (nc + 1);
+      const int64_t r = (int64_t)(hd[c] - hd[s * cps]) + (rr & 0xffff);
+      const int32_t rrow = slot_offset[p] + hist_p[(int64_t)p * (nc + 1) + c] + (rr >> 16);
+      out_r = rrow;
+      if (r >= cap) {
+        atomicOr(status, MOE_DEVICE_OVER_CAPACITY);
+        slot_rows[rrow] = -1;
+      } else {
+        drow = ((int64_t)d * S + s) * cap + r;
+        dpart = d;
+        out_d = (int32_t)drow;
+        slot_rows[rrow] = out_d;
+        tail_w = (uint32_t)lane | ((uint32_t)(slot_local[p] & 0xff) << 8) |
+                 ((event_id & 0xffffu) << 16);
+      }
+    }
+    disp_row[gi] = out_d;
+    ret_row[gi] = out_r;
+  }
+
+  // ---- load the token and quantize ----
+  uint4 raw[NIT][BF16 ? 2 : 4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int e0 = (i * 64 + lane) * 16;
+    if (e0 < H) {
+      if (BF16) {
+        const uint4 *src = (const uint4 *)((const uint16_t *)x + t * H + e0);
+        raw[i][0] = src[0];
+        raw[i][1] = src[1];
+        const uint32_t *w = (const uint32_t *)&raw[i][0];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffffu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+        }
+      } else {
+        const uint4 *src = (const uint4 *)((const float *)x + t * H + e0);
+#pragma unroll
+        for (int q = 0; q < (BF16 ? 2 : 4); ++q) raw[i][q] = src[q];
+        const float *f = (const float *)&raw[i][0];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(f[q]));
+      }
+    }
+  }
+  amax = wave_max_f32(amax);
+  const float scale = amax / 127.0f;
+
+  uint4 codes[NIT];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    float v[16];
+    if (BF16) {
+      const uint32_t *w = (const uint32_t *)&raw[i][0];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+        v[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+      }
+    } else {
+      const float *f = (const float *)&raw[i][0];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = f[q];
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int code = 0;
+        if (scale != 0.0f) {
+          float y = rintf(v[4 * q + r] / scale);
+          y = fminf(fmaxf(y, -127.0f), 127.0f);
+          code = (int)y;
+        }
+        word |= ((uint32_t)code & 0xffu) << (8 * r);
+      }
+      pk[q] = word;
+    }
+    codes[i] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+
+  // ---- k message copies ----
+  const int64_t relay_base = (int64_t)relays * S * cap;
+  for (int j = 0; j < k; ++j) {
+    const int64_t row = __shfl(drow, j, 64);
+    if (row < 0) continue;
+    const int d = __shfl(dpart, j, 64);
+    const uint32_t tw = __shfl(tail_w, j, 64);
+    uint8_t *dst = (relays > 0 && d >= relays) ? relay_buf + (row - relay_base) * msg
+                                               : disp_buf + row * msg;
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int e0 = (i * 64 + lane) * 16;
+      if (e0 < H) *(uint4 *)(dst + e0) = codes[i];
+    }
+    if (lane == 0)
+      *(uint4 *)(dst + H) = make_uint4(__float_as_uint(scale), (uint32_t)s, (uint32_t)b, tw);
+  }
+}
+
+// ---------------------------------------------------------------- relay ---
+// Second hop: each route whose partition is >= relays moves its message row
+// from the relay region to its final region (same region-relative row).
+__global__ __launch_bounds__(256) void dispatch_relay_kernel(
+    const int32_t *__restrict__ disp_row, int64_t n_routes, int64_t relay_base, int64_t msg,
+    const uint8_t *__restrict__ relay_buf, uint8_t *__restrict__ disp_buf) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gi >= n_routes) return;
+  const int64_t row = disp_row[gi];
+  if (row < relay_base) return;  // direct route (or dropped: -1)
+  const uint4 *src = (const uint4 *)(relay_buf + (row - relay_base) * msg);
+  uint4 *dst = (uint4 *)(disp_buf + row * msg);
+  for (int64_t i = lane; i < msg / 16; i += 64) dst[i] = src[i];
+}
+
+// Empty batch: meta = {event, 0, 0}, zero slot counts and offsets, clear status.
+__global__ void dispatch_empty_kernel(int D, int S, int P, uint32_t event_id,
+                                      moe_meta_t *__restrict__ meta,
+                                      int32_t *__restrict__ slot_count,
+                                      int32_t *__restrict__ slot_offset,
+                                      int32_t *__restrict__ status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nm = (int64_t)D * S;
+  if (i < nm) {
+    moe_meta_t m;
+    m.event_id = event_id;
+    m.offset = 0;
+    m.count = 0;
+    m.reserved = 0;
+    meta[i] = m;
+  } else if (i < nm + P) {
+    slot_count[i - nm] = 0;
+    slot_offset[i - nm] = 0;
+  } else if (i == nm + P) {
+    slot_offset[P] = 0;
+    *status = 0;
+  }
+}
+
+template <int NIT>
+void launch_scatter(bool bf16, dim3 grid, hipStream_t st, const void *x, const int32_t *phys,
+                    const int32_t *sp, const int32_t *sl, const int32_t *hd, const int32_t *hp,
+                    const int32_t *rr, const int32_t *so, const moe_geom_t &g, int ct, int cps,
+                    int nc, int64_t cap, int64_t msg, uint32_t ev, uint8_t *db, uint8_t *rb,
+                    int32_t *srows, int32_t *drow, int32_t *rrow, int32_t *status) {
+  if (bf16)
+    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, true>), grid, dim3(256), 0, st, x, phys, sp,
+                       sl, hd, hp, rr, so, g.T, g.H, g.k, g.S, g.LB, ct, cps, nc, cap, msg,
+                       g.relays, ev, db, rb, srows, drow, rrow, status);
+  else
+    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, false>), grid, dim3(256), 0, st, x, phys, sp,
+                       sl, hd, hp, rr, so, g.T, g.H, g.k, g.S, g.LB, ct, cps, nc, cap, msg,
+                       g.relays, ev, db, rb, srows, drow, rrow, status);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
+                               const int32_t *slot_partition, uint32_t event_id,
+                               const moe_geom_t *g, void *disp_buf, moe_meta_t *meta,
+                               int32_t *slot_count, int32_t *slot_offset, int32_t *slot_rows,
+                               int32_t *disp_row, int32_t *ret_row, void *relay_buf, void *scratch,
+                               size_t scratch_bytes, void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (!slot_partition || !meta || !slot_count || !slot_offset || !scratch) return MOE_ERR_INVALID_ARG;
+  if (g->T > 0 && (!x || !phys_ids || !disp_buf || !slot_rows || !disp_row || !ret_row))
+    return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(disp_buf) || !aligned16(scratch)) return MOE_ERR_INVALID_ARG;
+  if (g->T > 0 && g->relays > 0 && (!relay_buf || !aligned16(relay_buf))) return MOE_ERR_INVALID_ARG;
+  const DispatchScratch L = dispatch_scratch_layout(*g);
+  if ((int64_t)scratch_bytes < L.total) return MOE_ERR_CAPACITY;
+  if (g->T == 0) {
+    // empty batch: every count is zero, the layout is empty
+    const unsigned blocks = (unsigned)(((int64_t)g->D * g->S + g->P + 1 + 255) / 256);
+    hipLaunchKernelGGL(dispatch_empty_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       g->D, g->S, g->P, event_id, meta, slot_count, slot_offset,
+                       (int32_t *)((uint8_t *)scratch + L.status));
+    return launch_status();
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *sc = (uint8_t *)scratch;
+  int32_t *status = (int32_t *)(sc + L.status);
+  int32_t *hist_d = (int32_t *)(sc + L.hist_d);
+  int32_t *hist_p = (int32_t *)(sc + L.hist_p);
+  int32_t *route_rank = (int32_t *)(sc + L.route_rank);
+  int32_t *slot_local = (int32_t *)(sc + L.slot_local);
+  const int ct = chunk_tokens(*g);
+  const int cps = (int)chunks_per_source(*g);
+  const int nc = g->S * cps;
+  const int64_t cap = cap_of(*g), msg = msg_bytes_of(*g);
+
+  const size_t lds = sizeof(int32_t) * 4 * (g->D + g->P);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nc), dim3(256), lds, s, phys_ids, slot_partition,
+                     g->T, g->k, g->P, g->D, g->LB, ct, cps, nc, hist_d, hist_p, route_rank);
+  if ((st = launch_status()) != MOE_OK) return st;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(g->D + g->P), dim3(256), 0, s, hist_d, hist_p,
+                     g->D, nc);
+  if ((st = launch_status()) != MOE_OK) return st;
+  const unsigned fin_blocks = 1 + (unsigned)(((int64_t)g->D * g->S + 1023) / 1024);
+  hipLaunchKernelGGL(dispatch_finalize_kernel, dim3(fin_blocks), dim3(1024), 0, s, hist_d, hist_p,
+                     slot_partition, g->D, g->P, g->S, cps, nc, event_id, meta, slot_count,
+                     slot_offset, slot_local, status);
+  if ((st = launch_status()) != MOE_OK) return st;
+
+  const dim3 grid((unsigned)((g->T + 3) / 4));
+  const bool bf16 = x_dtype == MOE_DTYPE_BF16;
+  uint8_t *db = (uint8_t *)disp_buf, *rb = (uint8_t *)relay_buf;
+  const int nit = (g->H + 1023) / 1024;
+#define MOE_SCATTER(N)                                                                         \
+  launch_scatter<N>(bf16, grid, s, x, phys_ids, slot_partition, slot_local, hist_d, hist_p,     \
+                    route_rank, slot_offset, *g, ct, cps, nc, cap, msg, event_id, db, rb,        \
+                    slot_rows, disp_row, ret_row, status)
+  if (nit <= 1)
+    MOE_SCATTER(1);
+  else if (nit <= 2)
+    MOE_SCATTER(2);
+  else if (nit <= 4)
+    MOE_SCATTER(4);
+  else if (nit <= 8)
+    MOE_SCATTER(8);
+  else
+    MOE_SCATTER(16);
+#undef MOE_SCATTER
+  if ((st = launch_status()) != MOE_OK) return st;
+
+  if (g->relays > 0) {
+    const int64_t n = (int64_t)g->T * g->k;
+    hipLaunchKernelGGL(dispatch_relay_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s,
+                       disp_row, n, (int64_t)g->relays * g->S * cap, msg, rb, db);
+    if ((st = launch_status()) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}

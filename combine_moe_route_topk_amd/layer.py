@@ -1,0 +1,119 @@
+"""Static buffers and the composed MoE layer call sequence.
+
+``MoeBuffers`` allocates, once, every device buffer the C ABI needs, sized by
+``moe_plan_sizes`` (the static worst-case sizing of the dispatch regions:
+rank_num x local_batch x min(topK, experts per partition) x message size).
+``MoeLayer.forward`` enqueues the path on the current stream:
+route -> dispatch (+ second hop) -> experts (or identity) -> E2A hop -> combine.
+Nothing here computes: it allocates with torch and calls the library.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16,
+               RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_ffn_q8,
+               moe_plan_sizes, moe_relay_returns, moe_route_topk)
+
+
+class MoeBuffers:
+    def __init__(self, g: Geom, I: int = 0, out_dtype: torch.dtype = torch.bfloat16,
+                 device: str = "cuda"):
+        self.g = g
+        self.I = I
+        sz = moe_plan_sizes(g, I)
+        self.sizes = sz
+        T, k, H = g.T, g.k, g.H
+        i32 = dict(dtype=torch.int32, device=device)
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.disp_buf = torch.empty(sz.dispatch_bytes, **u8)
+        self.relay_buf = torch.empty(sz.relay_bytes, **u8) if g.relays else None
+        self.meta = torch.empty((g.D, g.S, 4), **i32)
+        self.slot_count = torch.empty(g.P, **i32)
+        self.slot_offset = torch.empty(g.P + 1, **i32)
+        self.slot_rows = torch.empty(T * k, **i32)
+        self.disp_row = torch.empty((T, k), **i32)
+        self.ret_row = torch.empty((T, k), **i32)
+        self.topk_ids = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.phys = torch.empty((T, k), **i32)
+        self.expert_counts = torch.empty(g.E, **i32)
+        self.dscratch = torch.empty(sz.dispatch_scratch_bytes, **u8)
+        self.fscratch = torch.empty(max(sz.ffn_scratch_bytes, 256), **u8)
+        nret = sz.return_bytes // (2 * H)
+        self.ret = torch.empty((nret, H), dtype=torch.int16, device=device)
+        self.comb_row = torch.empty((T, k), **i32) if g.relays else None
+        self.out = torch.empty((T, H), dtype=out_dtype, device=device)
+
+    def disp_rows_view(self):
+        """The dispatch buffer as [D*S*cap][msg] bytes."""
+        return self.disp_buf.view(-1, self.sizes.msg_bytes)
+
+    def device_status(self) -> int:
+        return int(self.dscratch[:4].view(torch.int32).item())
+
+
+class MoeLayer:
+    """One MoE layer: replica map + (optional) INT8 SwiGLU expert weights."""
+
+    def __init__(self, g: Geom, gating: str, slot_partition: torch.Tensor,
+                 slot_logical: torch.Tensor, replica_offsets: Optional[torch.Tensor] = None,
+                 replica_slots: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                 weights=None, I: int = 0, out_dtype: torch.dtype = torch.bfloat16):
+        self.g = g
+        self.gating = GATING_SOFTMAX if gating == "softmax" else GATING_SIGMOID
+        self.slot_partition = slot_partition
+        self.slot_logical = slot_logical
+        self.replica_offsets = replica_offsets
+        self.replica_slots = replica_slots
+        self.bias = bias
+        self.weights = weights  # (w_gateup, s_gateup, w_down, s_down) device tensors or None
+        self.I = I
+        self.out_dtype = out_dtype
+        self.buf = MoeBuffers(g, I, out_dtype)
+        self.event_id = 0
+
+    @staticmethod
+    def _dt(t: torch.Tensor) -> int:
+        return DTYPE_BF16 if t.dtype in (torch.bfloat16, torch.int16, torch.uint16) else DTYPE_F32
+
+    def route(self, logits):
+        b = self.buf
+        moe_route_topk(logits, self._dt(logits), self.bias, self.gating, self.replica_offsets,
+                       self.replica_slots, self.g, b.topk_ids, b.topk_w, b.phys, b.expert_counts)
+
+    def dispatch(self, x):
+        b = self.buf
+        self.event_id = (self.event_id + 1) & 0xFFFFFFFF
+        moe_dispatch_q8(x, self._dt(x), b.phys, self.slot_partition, self.event_id, self.g,
+                        b.disp_buf, b.meta, b.slot_count, b.slot_offset, b.slot_rows, b.disp_row,
+                        b.ret_row, b.relay_buf, b.dscratch)
+
+    def experts(self, acc_gateup_dbg=None, acc_down_dbg=None):
+        b = self.buf
+        wgu, sgu, wd, sd = self.weights
+        moe_expert_ffn_q8(b.disp_buf, b.slot_count, b.slot_offset, b.slot_rows, self.slot_logical,
+                          wgu, sgu, wd, sd, self.I, self.g, b.ret, acc_gateup_dbg, acc_down_dbg,
+                          b.fscratch)
+
+    def combine(self, mode: str):
+        b = self.buf
+        odt = DTYPE_BF16 if self.out_dtype == torch.bfloat16 else DTYPE_F32
+        if mode == "q8":
+            moe_combine(RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, b.topk_w, self.g, odt, b.out)
+        else:
+            row = b.ret_row
+            if self.g.relays:
+                moe_relay_returns(b.ret, b.phys, self.slot_partition, b.ret_row, self.g, b.comb_row)
+                row = b.comb_row
+            moe_combine(RET_BF16, b.ret, row, b.topk_w, self.g, odt, b.out)
+
+    def forward(self, x, logits, combine: str = "bf16"):
+        self.route(logits)
+        self.dispatch(x)
+        if self.weights is not None:
+            self.experts()
+        self.combine(combine)
+        return self.buf.out

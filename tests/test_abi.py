@@ -1,0 +1,131 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, sizes buffers per the static-buffer formula, rejects bad arguments
+before any launch, and its EPLB planner matches the oracle's."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import combine_moe_route_topk_amd as moe
+import moe_workloads as mw
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        txt = open(h).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(moe_\w+)\s*\(", txt, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    decl = _declared_symbols()
+    assert decl == set(moe.EXPORTED), decl ^ set(moe.EXPORTED)
+    for n in decl:
+        assert hasattr(L, n)
+    assert moe.status_string(moe.MOE_ERR_CAPACITY) == "capacity exceeded"
+
+
+def test_plan_sizes_reproduce_printed_static_buffers():
+    """CMI 缓冲区公式: 320 ranks, local batch 96, 1 expert per die, top-8 ->
+    225 MiB dispatch (7680-byte messages) and 420 MiB bf16 combine per die."""
+    g = moe.geom(T=320 * 96, H=7168, E=320, P=320, k=8, D=320, Epp=1, S=320, LB=96, msg_bytes=7680)
+    s = moe.moe_plan_sizes(g, 2048)
+    assert s.cap_rows == 96
+    assert s.dispatch_bytes_per_partition == 225 * 2 ** 20
+    assert s.combine_bytes_per_partition == 420 * 2 ** 20
+    assert s.dispatch_bytes == 320 * 225 * 2 ** 20
+    # default message: H + 16-byte trailer
+    g.msg_bytes = 0
+    s = moe.moe_plan_sizes(g, 0)
+    assert s.msg_bytes == 7184 and s.ffn_scratch_bytes == 0
+
+
+@pytest.mark.parametrize("name", list(mw.WORKLOADS))
+def test_plan_sizes_of_every_workload(name):
+    w = mw.WORKLOADS[name]
+    s = moe.moe_plan_sizes(moe.geom_of(w), w.I)
+    assert s.cap_rows == w.cap and s.msg_bytes == w.msg
+    assert s.dispatch_bytes == w.D * w.S * w.cap * w.msg
+    if w.relays:
+        assert s.relay_bytes == (w.D - w.relays) * w.S * w.cap * w.msg
+
+
+def test_invalid_arguments_rejected_before_launch():
+    """Host validation returns an error code and launches nothing (runs without a GPU)."""
+    L = moe.lib()
+    g = moe.geom(T=16, H=64, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    bad = moe.geom(T=15, H=64, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)  # T != S * LB
+    assert L.moe_route_topk(None, 0, None, 0, None, None, ctypes.byref(g), None, None, None, None,
+                            None) == moe.MOE_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_route_topk(fake, 0, None, 0, None, None, ctypes.byref(bad), fake, fake, fake,
+                            None, None) == moe.MOE_ERR_INVALID_ARG
+    odd = moe.geom(T=16, H=60, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    assert L.moe_combine(0, fake, fake, fake, ctypes.byref(odd), 0, fake, None) == moe.MOE_ERR_UNSUPPORTED
+    bigk = moe.geom(T=16, H=64, E=32, P=32, k=17, D=4, Epp=8, S=4, LB=4)
+    assert L.moe_combine(0, fake, fake, fake, ctypes.byref(bigk), 0, fake, None) == moe.MOE_ERR_UNSUPPORTED
+    # misaligned buffer
+    assert L.moe_combine(0, ctypes.c_void_p(0x1004), fake, fake, ctypes.byref(g), 0, fake,
+                         None) == moe.MOE_ERR_INVALID_ARG
+    # scratch too small
+    s = moe.moe_plan_sizes(g)
+    assert L.moe_dispatch_q8(fake, 0, fake, fake, 1, ctypes.byref(g), fake, fake, fake, fake, fake,
+                             fake, fake, None, fake, s.dispatch_scratch_bytes - 1,
+                             None) == moe.MOE_ERR_CAPACITY
+    # FFN needs H % 128 == 0 and I % 64 == 0
+    assert L.moe_expert_ffn_q8(fake, fake, fake, fake, fake, fake, fake, fake, fake, 96,
+                               ctypes.byref(g), fake, None, None, fake, 1 << 30,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    # relay hop without relays configured
+    assert L.moe_relay_returns(fake, fake, fake, fake, ctypes.byref(g), fake,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError):
+        moe.moe_plan_sizes(bad)
+
+
+@pytest.mark.parametrize("seed,E,slices,budget", [(0, 32, 4, 8), (1, 64, 3, 16), (2, 8, 1, 5)])
+def test_eplb_planner_matches_oracle(seed, E, slices, budget):
+    rng = np.random.default_rng(seed)
+    pop = np.exp(-1.1 * np.log(rng.permutation(E) + 1.0))
+    cnt = np.stack([rng.multinomial(3000, pop / pop.sum()) for _ in range(slices)]).astype(np.int64)
+    D = E // 2 + budget
+    prim = (np.arange(E) // 2).astype(np.int32)
+    free = np.r_[np.zeros(E // 2), np.ones(budget)].astype(np.int32)
+    ro, rs, sp, sl, sel = moe.moe_eplb_build_map(cnt, budget, D, prim, free)
+    o = oracle.eplb_plan(cnt, budget, D, prim, free)
+    assert np.array_equal(ro, o["replica_offsets"]) and np.array_equal(rs, o["replica_slots"])
+    assert np.array_equal(sp, o["slot_partition"]) and np.array_equal(sl, o["slot_logical"])
+    assert np.array_equal(sel, o["selected"][:budget])
+
+
+def test_eplb_planner_capacity_error():
+    cnt = np.array([[10, 1, 1, 1]], np.int64)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_eplb_build_map(cnt, 3, 2, np.array([0, 0, 1, 1]), np.array([1, 1]))
+    assert ei.value.status == moe.MOE_ERR_CAPACITY
+
+
+def test_eplb_planner_on_the_eplb_workload():
+    """The 4096-token EPLB workload: 32 redundant slots planned from the
+    calibration batch land on partitions 256..287 and match the oracle."""
+    w = mw.WORKLOADS["eplb4096"]
+    bias = mw.zipf_bias(w)
+    counts = np.stack([oracle.expert_counts(
+        oracle.route_topk(mw.logits(w, i), w.k, w.gating, bias, logits_bf16=True)[0], w.E)
+        for i in range(w.calib_slices)])
+    prim = np.arange(w.E, dtype=np.int32)
+    free = np.r_[np.zeros(w.E), np.ones(w.budget)].astype(np.int32)
+    ro, rs, sp, sl, sel = moe.moe_eplb_build_map(counts, w.budget, w.D, prim, free)
+    o = oracle.eplb_plan(counts, w.budget, w.D, prim, free)
+    assert np.array_equal(sl, o["slot_logical"]) and np.array_equal(sp, o["slot_partition"])
+    assert sorted(sp[w.E:].tolist()) == list(range(w.E, w.E + w.budget))
+    assert np.all(np.diff(o["tail"]) <= 1e-9)

@@ -1,0 +1,411 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the same
+seeded inputs.  Integer, byte and index results are compared bit for bit; fp32
+results within 1e-5 relative + 1e-6 absolute; bf16 within 1e-2 relative +
+1e-3 absolute (and, where both sides run the same fp32 operations, bit for bit).
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_topk_amd as moe
+import moe_workloads as mw
+import oracle
+from _parity import (BF16_ATOL, BF16_RTOL, FP32_ATOL, FP32_RTOL, assert_close, bf16_to_f32,
+                     calib_ids, dev_bits, gather_rows, host, replica_map, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+# a multi-source case with ragged chunks (LB = 100 -> chunks of 32, 32, 32, 4),
+# several slots per partition and a non-power-of-two partition count
+RAGGED = mw.Workload("ragged", T=3 * 100, H=384, E=40, P=40, k=8, D=10, Epp=4, S=3, LB=100,
+                     gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                     experts="identity", combine="q8", out_dtype="f32")
+# small expert-FFN case: skewed slots spanning several 128-row m-tiles, empty
+# slots and ragged tails; H and I span several 64-wide K steps and n-tiles
+FFN_SMALL = mw.Workload("ffn_small", T=2 * 200, H=512, E=12, P=12, k=4, D=6, Epp=2, S=2, LB=200,
+                        gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                        experts="swiglu", combine="bf16", out_dtype="bf16", I=192)
+# two-hop case: 4 sources, 12 destination partitions, the first 4 are relays
+TWOHOP_SMALL = mw.Workload("twohop_small", T=4 * 40, H=256, E=10, P=12, k=4, D=12, Epp=1, S=4,
+                           LB=40, gating="sigmoid", logits_dtype="bf16", x_dtype="bf16",
+                           zipf=False, experts="synthetic", combine="bf16", out_dtype="bf16",
+                           eplb="first32", budget=2, relays=4)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class Case:
+    """Everything one workload needs, on the host (oracle) and on the device."""
+
+    def __init__(self, w: mw.Workload, event_id: int = 0x1234):
+        _log(f"[case] {w.name} T={w.T} H={w.H} E={w.E} P={w.P} k={w.k} D={w.D} S={w.S}")
+        self.w = w
+        self.event_id = event_id
+        self.lg = mw.logits(w)
+        self.bias = mw.zipf_bias(w)
+        self.x = mw.hidden(w)
+        cal = calib_ids(w) if w.eplb == "plan" else None
+        self.ro, self.rs, self.sp, self.sl = replica_map(w, cal)
+        self.use_map = w.eplb != "none"
+        self.g = moe.geom_of(w)
+        self.layer = moe.MoeLayer(
+            self.g, w.gating, to_dev(self.sp), to_dev(self.sl),
+            to_dev(self.ro) if self.use_map else None, to_dev(self.rs) if self.use_map else None,
+            None if self.bias is None else to_dev(self.bias), None, w.I,
+            torch.bfloat16 if w.out_dtype == "bf16" else torch.float32)
+        self.lg_d = dev_bits(self.lg, w.logits_dtype == "bf16")
+        self.x_d = dev_bits(self.x, w.x_dtype == "bf16")
+
+    # oracle side
+    def oracle_route(self):
+        w = self.w
+        ids, sc, tw = oracle.route_topk(self.lg, w.k, w.gating, self.bias,
+                                        logits_bf16=w.logits_dtype == "bf16")
+        phys = oracle.eplb_phys(ids, w.LB, w.E, self.ro if self.use_map else None,
+                                self.rs if self.use_map else None)
+        return ids, tw, phys
+
+    def oracle_dispatch(self, phys):
+        w = self.w
+        q, s = oracle.quant_tokens(self.x, w.x_dtype == "bf16")
+        lay = oracle.dispatch_layout(w, phys, self.sp, self.event_id)
+        return q, s, lay
+
+
+def _check_route(c: Case):
+    w = c.w
+    c.layer.route(c.lg_d)
+    ids, tw, phys = c.oracle_route()
+    b = c.layer.buf
+    assert np.array_equal(host(b.topk_ids), ids), "topk ids"
+    assert np.array_equal(host(b.phys), phys), "physical ids"
+    assert_close(host(b.topk_w), tw, FP32_RTOL, FP32_ATOL, "topk weights")
+    assert np.array_equal(host(b.expert_counts), oracle.expert_counts(ids, w.E)), "expert counts"
+    return ids, tw, phys
+
+
+def _check_dispatch(c: Case, phys, row_sample=None):
+    w = c.w
+    b = c.layer.buf
+    c.layer.event_id = c.event_id - 1
+    c.layer.dispatch(c.x_d)
+    q, s, lay = c.oracle_dispatch(phys)
+    torch.cuda.synchronize()
+    assert b.device_status() == 0
+    meta = host(b.meta)
+    assert np.array_equal(meta[..., :3].view(np.uint32)[..., 0], lay["meta"][..., 0].view(np.uint32))
+    assert np.array_equal(meta[..., 1:3], lay["meta"][..., 1:3]), "meta offset/count"
+    assert np.array_equal(host(b.slot_count), lay["slot_count"])
+    assert np.array_equal(host(b.slot_offset), lay["slot_offset"])
+    assert np.array_equal(host(b.disp_row), lay["disp_row"]), "disp_row"
+    assert np.array_equal(host(b.ret_row), lay["ret_row"]), "ret_row"
+    assert np.array_equal(host(b.slot_rows), lay["slot_rows"]), "slot_rows"
+    n = w.H + 16
+    if row_sample is None:
+        exp = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
+        got = gather_rows(b, lay["disp_row"].ravel())
+        assert np.array_equal(got[:, :n], exp[:, :n]), "message rows"
+    else:
+        for t0, t1 in row_sample:
+            exp = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id, t0, t1)
+            got = gather_rows(b, lay["disp_row"][t0:t1].ravel())
+            assert np.array_equal(got[:, :n], exp[:, :n]), f"message rows of tokens [{t0}, {t1})"
+    return q, s, lay
+
+
+# ------------------------------------------------------------------ route ---
+
+@pytest.mark.parametrize("name", ["tiny", "decode96", "global12288", "eplb4096", "twohop46080"])
+def test_route_parity(name):
+    c = Case(mw.WORKLOADS[name])
+    _check_route(c)
+
+
+# --------------------------------------------------------------- dispatch ---
+
+@pytest.mark.parametrize("name", ["tiny", "decode96", "ragged"])
+def test_dispatch_parity_small(name):
+    w = RAGGED if name == "ragged" else mw.WORKLOADS[name]
+    c = Case(w)
+    _, _, phys = _check_route(c)
+    _check_dispatch(c, phys)
+
+
+def test_dispatch_parity_global12288_full():
+    """T=12288, 128 sources x 96 tokens, 128 partitions x 2 slots, Zipf skew: the
+    full layout and every one of the 98304 message rows."""
+    c = Case(mw.WORKLOADS["global12288"])
+    _, _, phys = _check_route(c)
+    _check_dispatch(c, phys)
+
+
+def test_dispatch_parity_eplb4096_full():
+    c = Case(mw.WORKLOADS["eplb4096"])
+    _, _, phys = _check_route(c)
+    _check_dispatch(c, phys)
+
+
+def test_dispatch_twohop_small_equals_direct():
+    """Two-hop (relays = 4): layout and rows equal the oracle's one-hop layout,
+    and a direct run (relays = 0) writes the same bytes."""
+    c = Case(TWOHOP_SMALL)
+    _, _, phys = _check_route(c)
+    _check_dispatch(c, phys)
+    direct = Case(TWOHOP_SMALL.scaled(relays=0))
+    _check_route(direct)
+    direct.layer.event_id = c.event_id - 1
+    direct.layer.dispatch(direct.x_d)
+    rows = host(c.layer.buf.disp_row).ravel()
+    assert np.array_equal(gather_rows(c.layer.buf, rows), gather_rows(direct.layer.buf, rows))
+
+
+def test_dispatch_twohop46080_full_layout_sampled_rows():
+    """46080 tokens from 160 sources to 288 partitions through 160 relays:
+    full layout, and the message rows of four token ranges (first, last, two inner)."""
+    c = Case(mw.WORKLOADS["twohop46080"])
+    _, _, phys = _check_route(c)
+    T = c.w.T
+    _check_dispatch(c, phys, row_sample=[(0, 512), (T // 3, T // 3 + 512), (T // 2 + 7, T // 2 + 300),
+                                         (T - 512, T)])
+
+
+def test_dispatch_is_deterministic():
+    c = Case(RAGGED)
+    c.layer.route(c.lg_d)
+    c.layer.dispatch(c.x_d)
+    b = c.layer.buf
+    a1 = [host(t).copy() for t in (b.disp_row, b.ret_row, b.slot_rows, b.meta)]
+    rows1 = gather_rows(b, a1[0].ravel())
+    c.layer.event_id -= 1
+    c.layer.dispatch(c.x_d)
+    a2 = [host(t) for t in (b.disp_row, b.ret_row, b.slot_rows, b.meta)]
+    for u, v in zip(a1, a2):
+        assert np.array_equal(u, v)
+    assert np.array_equal(rows1, gather_rows(b, a1[0].ravel()))
+
+
+# ---------------------------------------------------------------- combine ---
+
+@pytest.mark.parametrize("name", ["tiny", "decode96", "ragged"])
+def test_combine_q8_identity_experts(name):
+    """Identity experts: combine reads the dispatched INT8 rows back.  With the
+    oracle's fp32 weights the output is bit-identical to the oracle's; the
+    end-to-end output (GPU weights) is within the fp32 tolerance."""
+    w = RAGGED if name == "ragged" else mw.WORKLOADS[name]
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    b = c.layer.buf
+    rows = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    w32 = tw.astype(np.float32)
+    ref = oracle.combine(rows, ident, w32, w.k, w.H, "q8", False, scale_offset=w.H)
+    c.layer.combine("q8")
+    assert_close(host(b.out), ref, FP32_RTOL, FP32_ATOL, "combine end to end")
+    out2 = torch.empty_like(b.out)
+    moe.moe_combine(moe.RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, to_dev(w32), c.g,
+                    moe.DTYPE_F32, out2)
+    assert np.array_equal(host(out2), ref), "combine with identical weights is bit-exact"
+    # closed form: sum_j w_j dequant(quant(x)) ~ x
+    xf = bf16_to_f32(c.x) if w.x_dtype == "bf16" else c.x
+    assert np.all(np.abs(host(out2) - xf) <= s[:, None] * 0.5 + 1e-5 * np.abs(xf) + 1e-6)
+
+
+def test_combine_bf16_returns_global12288():
+    """Synthetic bf16 expert returns at T=12288: bf16 output bit-identical to the
+    oracle given the same fp32 weights, and within tolerance end to end."""
+    c = Case(mw.WORKLOADS["global12288"])
+    w = c.w
+    ids, tw, phys = _check_route(c)
+    c.layer.dispatch(c.x_d)
+    lay = oracle.dispatch_layout(w, phys, c.sp, 1)
+    b = c.layer.buf
+    torch.cuda.synchronize()
+    assert np.array_equal(host(b.ret_row), lay["ret_row"])
+    rets = mw.route_returns(w)
+    ret_d = torch.from_numpy(rets.view(np.int16)).cuda()
+    b.ret.index_copy_(0, torch.from_numpy(lay["ret_row"].ravel().astype(np.int64)).cuda(), ret_d)
+    del ret_d
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    w32 = tw.astype(np.float32)
+    ref = oracle.combine(rets, ident, w32, w.k, w.H, "bf16", True)
+    out2 = torch.empty_like(b.out)
+    moe.moe_combine(moe.RET_BF16, b.ret, b.ret_row, to_dev(w32), c.g, moe.DTYPE_BF16, out2)
+    assert np.array_equal(host(out2.view(torch.int16)).view(np.uint16), ref), "bf16 combine bits"
+    c.layer.combine("bf16")
+    assert_close(bf16_to_f32(host(b.out.view(torch.int16))), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL,
+                 "combine end to end")
+
+
+def test_combine_twohop_returns_equal_direct():
+    """E2A through relays gives the same bf16 output bits as reading the returns directly."""
+    c = Case(TWOHOP_SMALL)
+    w = c.w
+    ids, tw, phys = _check_route(c)
+    c.layer.dispatch(c.x_d)
+    b = c.layer.buf
+    rets = mw.route_returns(w)
+    rr = torch.from_numpy(host(b.ret_row).ravel().astype(np.int64)).cuda()
+    b.ret[: w.T * w.k].index_copy_(0, rr, torch.from_numpy(rets.view(np.int16)).cuda())
+    c.layer.combine("bf16")
+    relayed = host(b.out.view(torch.int16)).copy()
+    comb = host(b.comb_row)
+    n_rel = int((comb >= w.T * w.k).sum())
+    assert n_rel > 0, "some routes must go through a relay"
+    direct = torch.empty_like(b.out)
+    moe.moe_combine(moe.RET_BF16, b.ret, b.ret_row, b.topk_w, c.g, moe.DTYPE_BF16, direct)
+    assert np.array_equal(relayed, host(direct.view(torch.int16)))
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    ref = oracle.combine(rets, ident, host(b.topk_w), w.k, w.H, "bf16", True)
+    assert np.array_equal(relayed.view(np.uint16), ref)
+
+
+# ------------------------------------------------------------- expert FFN ---
+
+def _ffn_case(w):
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    wgu, sgu, wd, sd = mw.all_expert_weights(w)
+    c.layer.weights = (to_dev(wgu), to_dev(sgu), to_dev(wd), to_dev(sd))
+    c.layer.I = w.I
+    return c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd)
+
+
+def test_expert_ffn_parity_small():
+    """Grouped INT8 SwiGLU: int32 accumulators of both GEMMs bit-exact, and the
+    bf16 return rows bit-exact (the same fp32 epilogue on both sides)."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
+    sc = lay["slot_count"]
+    assert sc.max() > 256, "want a slot spanning three 128-row m-tiles"
+    n = w.T * w.k
+    acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
+    acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
+    c.layer.experts(acc_gu, acc_d)
+    torch.cuda.synchronize()
+    b = c.layer.buf
+    logical = c.sl[phys.ravel()]
+    ret = host(b.ret.view(torch.int16)).view(np.uint16)
+    agu, ad = host(acc_gu), host(acc_d)
+    rr = lay["ret_row"].ravel()
+    for e in np.unique(logical):
+        sel = np.nonzero(logical == e)[0]
+        toks = sel // w.k
+        y, hq, hs, o_gu, o_d = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e],
+                                                 want_acc=True)
+        assert np.array_equal(agu[rr[sel]], o_gu), f"gate/up accumulators, expert {e}"
+        assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
+        assert np.array_equal(ret[rr[sel]], y), f"return rows, expert {e}"
+
+
+def test_layer_ffn_small_end_to_end():
+    """route -> dispatch -> experts -> combine against the oracle's whole layer."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), _, weights = _ffn_case(w)
+    out = host(c.layer.forward(c.x_d, c.lg_d).view(torch.int16)).view(np.uint16)
+    r = oracle.moe_layer(w, c.x, c.lg, c.bias, None, None, c.sp, c.sl, event_id=1, weights=weights)
+    assert_close(bf16_to_f32(out), bf16_to_f32(r["out"]), BF16_RTOL, BF16_ATOL, "layer output")
+
+
+def test_expert_ffn_layer12288_sampled_rows():
+    """The headline layer (T=12288, 256 experts, I=2048, Zipf routing), launched as
+    the bench launches it; the oracle recomputes 32 rows of each of four slots
+    (the hottest, the least loaded non-empty and two random ones)."""
+    w = mw.WORKLOADS["layer12288"]
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    c.layer.dispatch(c.x_d)
+    q, s = oracle.quant_tokens(c.x, True)
+    lay = oracle.dispatch_layout(w, phys, c.sp, 1)
+    _log("[layer12288] generating weights")
+    wgu, sgu, wd, sd = mw.all_expert_weights(w)
+    c.layer.weights = (to_dev(wgu), to_dev(sgu), to_dev(wd), to_dev(sd))
+    c.layer.experts()
+    torch.cuda.synchronize()
+    b = c.layer.buf
+    assert np.array_equal(host(b.ret_row), lay["ret_row"])
+    ret = host(b.ret.view(torch.int16)).view(np.uint16)
+    sc = lay["slot_count"]
+    nz = np.nonzero(sc)[0]
+    rng = np.random.default_rng(0)
+    slots = {int(np.argmax(sc)), int(nz[np.argmin(sc[nz])])} | set(rng.choice(nz, 2).tolist())
+    inv = np.argsort(lay["ret_row"].ravel())  # ret row -> route index
+    for p in sorted(slots):
+        o = lay["slot_offset"][p]
+        rows = np.arange(o, o + sc[p])
+        if len(rows) > 32:
+            rows = np.sort(rng.choice(rows, 32, replace=False))
+        routes = inv[rows]
+        toks = routes // w.k
+        e = c.sl[p]
+        y, *_ = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e])
+        assert np.array_equal(ret[rows], y), f"slot {p} (expert {e}, {sc[p]} rows)"
+
+
+# ------------------------------------------------------------ edge cases ---
+
+def test_empty_batch():
+    """T = 0 (every source partition sends nothing): all entry points succeed,
+    meta counts and slot counts are zero, the expert histogram is zero."""
+    w = mw.WORKLOADS["tiny"].scaled(name="empty", T=0, LB=0)
+    c = Case(w)
+    c.layer.buf.meta.fill_(-7)
+    c.layer.buf.slot_count.fill_(-7)
+    c.layer.buf.expert_counts.fill_(-7)
+    c.layer.route(c.lg_d)
+    c.layer.dispatch(c.x_d)
+    c.layer.combine("q8")
+    torch.cuda.synchronize()
+    b = c.layer.buf
+    assert np.all(host(b.meta)[..., 1:3] == 0) and np.all(host(b.slot_count) == 0)
+    assert np.all(host(b.slot_offset) == 0) and np.all(host(b.expert_counts) == 0)
+    assert b.device_status() == 0
+
+
+def test_single_token_and_zero_token():
+    """One token per source, one of them all-zero: scale 0, codes 0, output 0."""
+    w = mw.WORKLOADS["tiny"].scaled(name="one", T=4, LB=1)
+    c = Case(w)
+    c.x[2] = 0
+    c.x_d = dev_bits(c.x, False)
+    _, _, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    assert s[2] == 0 and np.all(q[2] == 0)
+    c.layer.combine("q8")
+    assert np.all(host(c.layer.buf.out)[2] == 0)
+
+
+def test_invalid_routes_are_flagged_not_written():
+    """Out-of-range physical ids are dropped (row indices -1) and reported in the
+    device status word; nothing is written out of bounds."""
+    c = Case(RAGGED)
+    c.layer.route(c.lg_d)
+    b = c.layer.buf
+    b.phys[5, 3] = 10_000
+    b.phys[7, 0] = -3
+    c.layer.dispatch(c.x_d)
+    torch.cuda.synchronize()
+    assert b.device_status() & moe.MOE_DEVICE_BAD_ROUTE
+    dr = host(b.disp_row)
+    assert dr[5, 3] == -1 and dr[7, 0] == -1
+    assert int(host(b.meta)[..., 2].sum()) == c.w.T * c.w.k - 2
+
+
+def test_all_tokens_to_one_partition():
+    """Every route of every token lands on partition 0 (its Epp slots): regions
+    fill to exactly cap rows."""
+    w = RAGGED.scaled(name="hot", D=10, Epp=4)
+    c = Case(w)
+    lg = np.full((w.T, w.E), -5.0, np.float32)
+    lg[:, :w.k] = np.linspace(3, 1, w.k)  # experts 0..k-1 win everywhere
+    c.lg = mw.to_bf16_bits(lg)
+    c.lg_d = dev_bits(c.lg, True)
+    c.bias = None
+    c.layer.bias = None
+    # slots 0..3 on partition 0, 4..7 on partition 1 -> cap = LB * min(k, Epp) = 400 per region
+    _, _, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    assert lay["meta"][0, :, 2].max() == w.LB * min(w.k, w.Epp)
