@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE hot path on one MI355X.
+
+One step = one pass of the whole path over one batch, every stage in the
+library's HIP kernels: gate top-k routing -> INT8 quantization fused into the
+dispatch scatter -> grouped INT8 SwiGLU experts (gate/up stage, then
+requant + down stage) -> combine of the bf16 returns.  The workload is the
+12288-token layer (128 source partitions x 96 tokens, H=7168, 256 experts on
+128 partitions x 2, top-8, I=2048, sigmoid gate with a seeded log-Zipf skew),
+inputs resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s of the layer (value), dispatch+combine GB/s and
+its fraction of the 8 TB/s HBM peak, per-stage times, the roofline of the
+dominant kernel (the gate/up INT8 GEMM) and the CPU oracle's throughput on a
+bounded sample of the same workload (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(w):
+    """Bytes / ops each stage must move or compute (never capacity or padding)."""
+    T, H, E, k, I = w.T, w.H, w.E, w.k, w.I
+    R = T * k
+    return {
+        # read logits (bf16) + write ids, weights, physical ids
+        "route_bytes": T * E * 2 + R * 12,
+        # read x (bf16) and phys ids, write the k messages (H + 16 B each),
+        # the three row-index arrays and the (d, s) metadata
+        "dispatch_bytes": T * H * 2 + R * 4 + R * (H + 16) + 3 * R * 4 + w.D * w.S * 16,
+        # read bf16 returns, row ids and weights, write the bf16 output
+        "combine_bytes": R * H * 2 + R * 8 + T * H * 2,
+        # 2 ops per multiply-add: gate and up (2I outputs over K = H), down (H outputs over K = I)
+        "gateup_ops": 2 * R * H * 2 * I,
+        "down_ops": 2 * R * I * H,
+    }
+
+
+def build_layer(w, log_every=64):
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import combine_moe_route_topk_amd as moe
+    import moe_workloads as mw
+
+    t0 = time.time()
+    x = torch.from_numpy(mw.hidden(w).view(np.int16)).view(torch.bfloat16).cuda()
+    lg = torch.from_numpy(mw.logits(w).view(np.int16)).view(torch.bfloat16).cuda()
+    bias = torch.from_numpy(mw.zipf_bias(w)).cuda()
+    ro, rs, sp, sl = mw.identity_map(w)
+    dev = dict(device="cuda")
+    wgu = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.int8, **dev)
+    sgu = torch.empty((w.E, 2 * w.I), dtype=torch.float32, **dev)
+    wd = torch.empty((w.E, w.H, w.I), dtype=torch.int8, **dev)
+    sd = torch.empty((w.E, w.H), dtype=torch.float32, **dev)
+
+    def fill(e):
+        a, b, c, d = mw.expert_weights(w, e)
+        wgu[e].copy_(torch.from_numpy(a))
+        sgu[e].copy_(torch.from_numpy(b))
+        wd[e].copy_(torch.from_numpy(c))
+        sd[e].copy_(torch.from_numpy(d))
+        if e % log_every == 0:
+            log(f"[bench] weights of expert {e} generated ({time.time() - t0:.1f}s)")
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(fill, range(w.E)))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs and weights resident in HBM ({time.time() - t0:.1f}s)")
+    layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
+                         torch.from_numpy(sl).cuda(), bias=bias, weights=(wgu, sgu, wd, sd),
+                         I=w.I, out_dtype=torch.bfloat16)
+    return layer, x, lg
+
+
+def time_gpu(layer, x, lg, steps, warmup):
+    import torch
+    stages = [("route", lambda: layer.route(lg)),
+              ("dispatch", lambda: layer.dispatch(x)),
+              ("gateup", layer.experts_gateup),
+              ("down", layer.experts_down),
+              ("combine", lambda: layer.combine("bf16"))]
+    for _ in range(warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(steps):
+        for (name, f), (a, b) in zip(stages, ev[s]):
+            a.record()
+            f()
+            b.record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
+           for i, (name, _) in enumerate(stages)}
+    return total_ms / steps, per
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it stands, on the host cores: route, quantization, dispatch
+    layout and messages, and combine over the whole batch; the expert FFN on a
+    seeded sample of routes, scaled by route count."""
+    import numpy as np
+
+    import moe_workloads as mw
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS"):
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    oracle.set_threads(threads)
+    x, lg, bias = mw.hidden(w), mw.logits(w), mw.zipf_bias(w)
+    ro, rs, sp, sl = mw.identity_map(w)
+    t = {}
+    c0 = time.perf_counter()
+    ids, sc, tw = oracle.route_topk(lg, w.k, w.gating, bias, logits_bf16=True)
+    phys = oracle.eplb_phys(ids, w.LB, w.E)
+    t["route"] = time.perf_counter() - c0
+    c0 = time.perf_counter()
+    q, s = oracle.quant_tokens(x, True)
+    lay = oracle.dispatch_layout(w, phys, sp, 1)
+    rows = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], 1)
+    t["dispatch"] = time.perf_counter() - c0
+    del rows
+    rets = np.full((w.T * w.k, w.H), 0x3F80, np.uint16)  # timing does not depend on the values
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    c0 = time.perf_counter()
+    oracle.combine(rets, ident, tw.astype(np.float32), w.k, w.H, "bf16", True)
+    t["combine"] = time.perf_counter() - c0
+    del rets
+    # expert FFN: seeded sample of routes of one expert at a time, grown to fill the budget
+    rng = np.random.default_rng(0)
+    logical = sl[phys.ravel()]
+    hot = int(np.bincount(logical).argmax())
+    n_done, ffn_s, experts = 0, 0.0, []
+    spent = sum(t.values())
+    n = 16
+    while ffn_s < max(2.0, budget_s - spent) and n_done < 4096:
+        e = hot if not experts else int(rng.choice(np.unique(logical)))
+        sel = np.nonzero(logical == e)[0]
+        sel = rng.choice(sel, min(n, len(sel)), replace=False)
+        wgu, sgu, wd, sd = mw.expert_weights(w, e)
+        toks = sel // w.k
+        c0 = time.perf_counter()
+        oracle.expert_ffn(q[toks], s[toks], wgu, sgu, wd, sd)
+        ffn_s += time.perf_counter() - c0
+        n_done += len(sel)
+        experts.append(e)
+        n *= 2
+    t["ffn"] = ffn_s / n_done * w.T * w.k
+    total = sum(t.values())
+    return {
+        "value": w.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"route, quantization, dispatch layout + messages and combine over all "
+                   f"{w.T} tokens; expert FFN on {n_done} sampled routes of {len(experts)} "
+                   f"experts (hottest first), scaled by route count to {w.T * w.k} routes"),
+        "seconds": {k: round(v, 3) for k, v in t.items()},
+        "ffn_sample_seconds": round(ffn_s, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer12288")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
+              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_workloads as mw
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    w = mw.WORKLOADS[args.workload]
+    A = algorithmic(w)
+    layer, x, lg = build_layer(w)
+    ms, per = time_gpu(layer, x, lg, args.steps, args.warmup)
+    log(f"[bench] {ms:.3f} ms/step " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per.items()))
+
+    dc_bytes = A["dispatch_bytes"] + A["combine_bytes"]
+    dc_ms = per["dispatch"] + per["combine"]
+    dc_gbs = dc_bytes / (dc_ms * 1e-3) / 1e9
+    gu_tops = A["gateup_ops"] / (per["gateup"] * 1e-3) / 1e12
+    dn_tops = A["down_ops"] / (per["down"] * 1e-3) / 1e12
+    stages = {
+        "route": {"us": per["route"] * 1e3,
+                  "GBps": A["route_bytes"] / (per["route"] * 1e-3) / 1e9},
+        "dispatch": {"us": per["dispatch"] * 1e3,
+                     "GBps": A["dispatch_bytes"] / (per["dispatch"] * 1e-3) / 1e9},
+        "gateup": {"us": per["gateup"] * 1e3, "TOPS": gu_tops},
+        "down": {"us": per["down"] * 1e3, "TOPS": dn_tops},
+        "combine": {"us": per["combine"] * 1e3,
+                    "GBps": A["combine_bytes"] / (per["combine"] * 1e-3) / 1e9},
+    }
+    for v in stages.values():
+        for kk in list(v):
+            v[kk] = round(v[kk], 2)
+    result = {
+        "metric": "MoE dispatch+combine GB/s (% of HBM peak) and MoE-layer tokens/s, T=12288 H=7168 k=8",
+        "value": round(w.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
+                   "sources": f"{w.S}x{w.LB}", "partitions": f"{w.D}x{w.Epp}",
+                   "routing": "sigmoid(bf16 logit + log-Zipf(1.1) bias)",
+                   "parallelism": "one GPU, virtual partitions"},
+        "dispatch_combine": {"GBps": round(dc_gbs, 1), "frac_hbm_peak": round(dc_gbs / HBM_PEAK_GBS, 4),
+                             "bytes": dc_bytes, "us": round(dc_ms * 1e3, 2)},
+        "stages": stages,
+        "roofline": {"kernel": "ffn_gemm_kernel<GATEUP> (moe_expert_gateup_q8)",
+                     "bound": "mfma", "achieved": round(gu_tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "ops": "int8 multiply-adds x 2",
+                     "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

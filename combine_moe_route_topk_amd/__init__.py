@@ -30,7 +30,8 @@ GATING_SOFTMAX, GATING_SIGMOID = 0, 1
 RET_Q8_FROM_DISPATCH, RET_BF16 = 0, 1
 
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
-            "moe_expert_ffn_q8", "moe_relay_returns", "moe_combine", "moe_status_string")
+            "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8", "moe_relay_returns",
+            "moe_combine", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -79,6 +80,10 @@ def lib():
                                       _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_ffn_q8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                         ctypes.POINTER(Geom), _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_expert_gateup_q8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, ctypes.POINTER(Geom),
+                                           _P, _P, ctypes.c_size_t, _P]
+        L.moe_expert_down_q8.argtypes = [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(Geom), _P, _P, _P,
+                                         ctypes.c_size_t, _P]
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -178,6 +183,24 @@ def moe_expert_ffn_q8(disp_buf, slot_count, slot_offset, slot_rows, slot_logical
                                    _ptr(ret), _ptr(acc_gateup_dbg), _ptr(acc_down_dbg),
                                    _ptr(scratch), scratch.numel() * scratch.element_size(),
                                    _stream(stream)), "moe_expert_ffn_q8")
+
+
+def moe_expert_gateup_q8(disp_buf, slot_count, slot_offset, slot_rows, slot_logical, w_gateup,
+                         s_gateup, I: int, g: Geom, acc_gateup_dbg=None, scratch=None, stream=None):
+    _check(lib().moe_expert_gateup_q8(_ptr(disp_buf), _ptr(slot_count), _ptr(slot_offset),
+                                      _ptr(slot_rows), _ptr(slot_logical), _ptr(w_gateup),
+                                      _ptr(s_gateup), I, ctypes.byref(g), _ptr(acc_gateup_dbg),
+                                      _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                      _stream(stream)), "moe_expert_gateup_q8")
+
+
+def moe_expert_down_q8(slot_count, slot_offset, slot_logical, w_down, s_down, I: int, g: Geom, ret,
+                       acc_down_dbg=None, scratch=None, stream=None):
+    _check(lib().moe_expert_down_q8(_ptr(slot_count), _ptr(slot_offset), _ptr(slot_logical),
+                                    _ptr(w_down), _ptr(s_down), I, ctypes.byref(g), _ptr(ret),
+                                    _ptr(acc_down_dbg), _ptr(scratch),
+                                    scratch.numel() * scratch.element_size(), _stream(stream)),
+           "moe_expert_down_q8")
 
 
 def moe_relay_returns(ret, phys_ids, slot_partition, ret_row, g: Geom, comb_row, stream=None):

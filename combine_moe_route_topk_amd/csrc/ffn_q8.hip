@@ -331,6 +331,96 @@ __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restric
 
 using namespace moe;
 
+namespace moe {
+namespace {
+
+struct FfnArgs {
+  FfnScratch L;
+  int32_t *tiles;
+  float *pmax, *h, *hs;
+  int8_t *hq;
+  int64_t nrows, msg, mt_bound;
+};
+
+int ffn_common(const moe_geom_t *g, int32_t I, void *scratch, size_t scratch_bytes, FfnArgs *a) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (I <= 0 || I % 64 != 0 || I > 16384 || g->H % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!scratch || !aligned16(scratch)) return MOE_ERR_INVALID_ARG;
+  const FfnScratch L = ffn_scratch_layout(*g, I);
+  if ((int64_t)scratch_bytes < L.total) return MOE_ERR_CAPACITY;
+  uint8_t *sc = (uint8_t *)scratch;
+  *a = FfnArgs{L,
+                  (int32_t *)(sc + L.tiles),
+                  (float *)(sc + L.pmax),
+                  (float *)(sc + L.h),
+                  (float *)(sc + L.hs),
+                  (int8_t *)(sc + L.hq),
+                  (int64_t)g->T * g->k,
+                  msg_bytes_of(*g),
+                  (int64_t)g->T * g->k / BM + g->P};
+  return MOE_OK;
+}
+
+dim3 gemm_grid(int64_t mt_bound, int NT) {
+  int64_t gsz = mt_bound * NT;  // upper bound of sum_p ceil(n_p / BM) * NT
+  gsz = (gsz + kXcds - 1) / kXcds * kXcds;
+  return dim3((unsigned)gsz);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_count,
+                                    const int32_t *slot_offset, const int32_t *slot_rows,
+                                    const int32_t *slot_logical, const int8_t *w_gateup,
+                                    const float *s_gateup, int32_t I, const moe_geom_t *g,
+                                    int32_t *acc_gateup_dbg, void *scratch, size_t scratch_bytes,
+                                    void *stream) {
+  FfnArgs args{};
+  FfnArgs *a = &args;
+  int st = ffn_common(g, I, scratch, scratch_bytes, a);
+  if (st != MOE_OK) return st;
+  if (a->nrows == 0) return MOE_OK;
+  if (!disp_buf || !slot_count || !slot_offset || !slot_rows || !slot_logical || !w_gateup ||
+      !s_gateup)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(disp_buf) || !aligned16(w_gateup)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->tiles);
+  if ((st = launch_status()) != MOE_OK) return st;
+  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP>), gemm_grid(a->mt_bound, I / 64), dim3(256), 0, s,
+                     a->tiles, slot_count, slot_offset, slot_logical, slot_rows,
+                     (const uint8_t *)disp_buf, a->msg, (const int8_t *)nullptr,
+                     (const float *)nullptr, w_gateup, s_gateup, g->P, g->E, g->H, I, a->nrows,
+                     a->h, a->pmax, (uint16_t *)nullptr, acc_gateup_dbg);
+  return launch_status();
+}
+
+extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
+                                  const int32_t *slot_logical, const int8_t *w_down,
+                                  const float *s_down, int32_t I, const moe_geom_t *g,
+                                  uint16_t *ret, int32_t *acc_down_dbg, void *scratch,
+                                  size_t scratch_bytes, void *stream) {
+  FfnArgs args{};
+  FfnArgs *a = &args;
+  int st = ffn_common(g, I, scratch, scratch_bytes, a);
+  if (st != MOE_OK) return st;
+  if (a->nrows == 0) return MOE_OK;
+  if (!slot_count || !slot_offset || !slot_logical || !w_down || !s_down || !ret)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_down) || !aligned16(ret)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(ffn_requant_kernel, dim3((unsigned)((a->nrows + 3) / 4)), dim3(256), 0, s,
+                     a->h, a->pmax, slot_offset, g->P, I, a->nrows, a->hq, a->hs);
+  if ((st = launch_status()) != MOE_OK) return st;
+  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN>), gemm_grid(a->mt_bound, g->H / BN), dim3(256), 0, s,
+                     a->tiles, slot_count, slot_offset, slot_logical, (const int32_t *)nullptr,
+                     (const uint8_t *)nullptr, a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E,
+                     g->H, I, a->nrows, (float *)nullptr, (float *)nullptr, ret, acc_down_dbg);
+  return launch_status();
+}
+
 extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count,
                                  const int32_t *slot_offset, const int32_t *slot_rows,
                                  const int32_t *slot_logical, const int8_t *w_gateup,
@@ -338,51 +428,11 @@ extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count
                                  int32_t I, const moe_geom_t *g, uint16_t *ret,
                                  int32_t *acc_gateup_dbg, int32_t *acc_down_dbg, void *scratch,
                                  size_t scratch_bytes, void *stream) {
-  int st = validate_geom(g);
+  if (g && g->T > 0 && (!w_down || !s_down || !ret)) return MOE_ERR_INVALID_ARG;
+  int st = moe_expert_gateup_q8(disp_buf, slot_count, slot_offset, slot_rows, slot_logical,
+                                w_gateup, s_gateup, I, g, acc_gateup_dbg, scratch, scratch_bytes,
+                                stream);
   if (st != MOE_OK) return st;
-  if (!disp_buf || !slot_count || !slot_offset || !slot_rows || !slot_logical || !w_gateup ||
-      !s_gateup || !w_down || !s_down || !ret || !scratch)
-    return MOE_ERR_INVALID_ARG;
-  if (I <= 0 || I % 64 != 0 || I > 16384 || g->H % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (!aligned16(disp_buf) || !aligned16(w_gateup) || !aligned16(w_down) || !aligned16(ret) ||
-      !aligned16(scratch))
-    return MOE_ERR_INVALID_ARG;
-  const FfnScratch L = ffn_scratch_layout(*g, I);
-  if ((int64_t)scratch_bytes < L.total) return MOE_ERR_CAPACITY;
-  const int64_t nrows = (int64_t)g->T * g->k;
-  if (nrows == 0) return MOE_OK;
-
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t *sc = (uint8_t *)scratch;
-  int32_t *tiles = (int32_t *)(sc + L.tiles);
-  float *pmax = (float *)(sc + L.pmax);
-  float *h = (float *)(sc + L.h);
-  int8_t *hq = (int8_t *)(sc + L.hq);
-  float *hs = (float *)(sc + L.hs);
-  const int64_t msg = msg_bytes_of(*g);
-  const int P = g->P;
-
-  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, P, tiles);
-  if ((st = launch_status()) != MOE_OK) return st;
-
-  // upper bound of the m-tiles: sum_p ceil(n_p / BM) <= nrows / BM + P
-  const int64_t mt_bound = nrows / BM + P;
-  auto grid_for = [&](int NT) {
-    int64_t gsz = mt_bound * NT;
-    gsz = (gsz + kXcds - 1) / kXcds * kXcds;
-    return dim3((unsigned)gsz);
-  };
-  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP>), grid_for(I / 64), dim3(256), 0, s, tiles,
-                     slot_count, slot_offset, slot_logical, slot_rows, (const uint8_t *)disp_buf,
-                     msg, (const int8_t *)nullptr, (const float *)nullptr, w_gateup, s_gateup, P,
-                     g->E, g->H, I, nrows, h, pmax, (uint16_t *)nullptr, acc_gateup_dbg);
-  if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL(ffn_requant_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, h,
-                     pmax, slot_offset, P, I, nrows, hq, hs);
-  if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN>), grid_for(g->H / BN), dim3(256), 0, s, tiles,
-                     slot_count, slot_offset, slot_logical, slot_rows, (const uint8_t *)disp_buf,
-                     msg, hq, hs, w_down, s_down, P, g->E, g->H, I, nrows, (float *)nullptr,
-                     (float *)nullptr, ret, acc_down_dbg);
-  return launch_status();
+  return moe_expert_down_q8(slot_count, slot_offset, slot_logical, w_down, s_down, I, g, ret,
+                            acc_down_dbg, scratch, scratch_bytes, stream);
 }

@@ -14,8 +14,9 @@ from typing import Optional
 import torch
 
 from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16,
-               RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_ffn_q8,
-               moe_plan_sizes, moe_relay_returns, moe_route_topk)
+               RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_down_q8,
+               moe_expert_ffn_q8, moe_expert_gateup_q8, moe_plan_sizes, moe_relay_returns,
+               moe_route_topk)
 
 
 class MoeBuffers:
@@ -97,6 +98,18 @@ class MoeLayer:
         moe_expert_ffn_q8(b.disp_buf, b.slot_count, b.slot_offset, b.slot_rows, self.slot_logical,
                           wgu, sgu, wd, sd, self.I, self.g, b.ret, acc_gateup_dbg, acc_down_dbg,
                           b.fscratch)
+
+    def experts_gateup(self):
+        b = self.buf
+        wgu, sgu, _, _ = self.weights
+        moe_expert_gateup_q8(b.disp_buf, b.slot_count, b.slot_offset, b.slot_rows,
+                             self.slot_logical, wgu, sgu, self.I, self.g, None, b.fscratch)
+
+    def experts_down(self):
+        b = self.buf
+        _, _, wd, sd = self.weights
+        moe_expert_down_q8(b.slot_count, b.slot_offset, self.slot_logical, wd, sd, self.I, self.g,
+                           b.ret, None, b.fscratch)
 
     def combine(self, mode: str):
         b = self.buf

@@ -240,6 +240,28 @@ int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count, const int
                       size_t scratch_bytes, void *stream);
 
 /*
+ * The two stages of moe_expert_ffn_q8, for callers that schedule or time them
+ * apart [XDS DeepSeek INT8 量化, P085, P088]; moe_expert_ffn_q8 is exactly
+ * moe_expert_gateup_q8 followed by moe_expert_down_q8 on the same scratch.
+ *   moe_expert_gateup_q8: the fused gate/up QMM and the SwiGLU epilogue; leaves h
+ *     (fp32) and its per-row partial maxima in scratch.
+ *   moe_expert_down_q8: token-wise INT8 of h (hq, hs) and the down QMM into ret.
+ *     It must follow moe_expert_gateup_q8 on the same stream, scratch, geometry
+ *     and slot arrays.
+ * Arguments have the meaning given for moe_expert_ffn_q8.
+ */
+int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_count,
+                         const int32_t *slot_offset, const int32_t *slot_rows,
+                         const int32_t *slot_logical, const int8_t *w_gateup,
+                         const float *s_gateup, int32_t I, const moe_geom_t *g,
+                         int32_t *acc_gateup_dbg, void *scratch, size_t scratch_bytes,
+                         void *stream);
+int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
+                       const int32_t *slot_logical, const int8_t *w_down, const float *s_down,
+                       int32_t I, const moe_geom_t *g, uint16_t *ret, int32_t *acc_down_dbg,
+                       void *scratch, size_t scratch_bytes, void *stream);
+
+/*
  * moe_relay_returns -- E2A second hop of the two-hop trampoline [XDS 解耦 A2A,
  * P045, Fig. 8: E2A runs the A2E path in reverse].  With g->relays = R > 0, the
  * return row of every route whose slot lives on a partition d >= R is copied

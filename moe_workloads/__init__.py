@@ -171,10 +171,11 @@ def route_returns(w: Workload, rows: Optional[np.ndarray] = None) -> np.ndarray:
 def _int8_uniform127(rng: np.random.Generator, shape) -> np.ndarray:
     """int8 uniform on [-127, 127] (the value -128 is redrawn)."""
     n = int(np.prod(shape))
-    a = np.frombuffer(rng.bytes(n), dtype=np.int8).copy()
+    bg = rng.bit_generator
+    a = bg.random_raw((n + 7) // 8).view(np.int8)[:n].copy()
     bad = np.flatnonzero(a == -128)
     while bad.size:
-        a[bad] = np.frombuffer(rng.bytes(bad.size), dtype=np.int8)
+        a[bad] = bg.random_raw((bad.size + 7) // 8).view(np.int8)[:bad.size]
         bad = bad[a[bad] == -128]
     return a.reshape(shape)
 

@@ -47,6 +47,8 @@ def lib():
 
 
 def _p(a: Optional[np.ndarray]):
+    """Address of an array the caller keeps referenced for the duration of the call
+    (never pass a temporary: ctypes does not hold it alive)."""
     if a is None:
         return None
     assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
@@ -138,9 +140,11 @@ def dispatch_rows(w, q, scale, phys, slot_local, event_id: int, t0: int = 0, t1:
     g = geom_array(w)
     t1 = w.T if t1 is None else t1
     rows = np.empty(((t1 - t0) * w.k, w.msg), np.uint8)
-    _check(lib().orc_dispatch_rows(_p(g), _p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(scale)),
-                                   _p(np.ascontiguousarray(phys, np.int32)),
-                                   _p(np.ascontiguousarray(slot_local, np.int32)),
+    q = np.ascontiguousarray(q, np.int8)
+    scale = np.ascontiguousarray(scale, np.float32)
+    phys = np.ascontiguousarray(phys, np.int32)
+    slot_local = np.ascontiguousarray(slot_local, np.int32)
+    _check(lib().orc_dispatch_rows(_p(g), _p(q), _p(scale), _p(phys), _p(slot_local),
                                    event_id & 0xFFFFFFFF, t0, t1, _p(rows)), "dispatch_rows")
     return rows
 
@@ -156,9 +160,12 @@ def expert_ffn(q_rows, s_rows, wgu, sgu, wd, sd, want_acc: bool = False):
     hs = np.empty(n, np.float32)
     acc_gu = np.empty((n, 2 * I), np.int32) if want_acc else None
     acc_d = np.empty((n, H), np.int32) if want_acc else None
-    _check(lib().orc_expert_ffn(n, H, I, _p(q_rows), _p(s_rows), _p(np.ascontiguousarray(wgu)),
-                                _p(np.ascontiguousarray(sgu)), _p(np.ascontiguousarray(wd)),
-                                _p(np.ascontiguousarray(sd)), _p(acc_gu), _p(hq), _p(hs), _p(acc_d),
+    wgu = np.ascontiguousarray(wgu, np.int8)
+    sgu = np.ascontiguousarray(sgu, np.float32)
+    wd = np.ascontiguousarray(wd, np.int8)
+    sd = np.ascontiguousarray(sd, np.float32)
+    _check(lib().orc_expert_ffn(n, H, I, _p(q_rows), _p(s_rows), _p(wgu), _p(sgu), _p(wd),
+                                _p(sd), _p(acc_gu), _p(hq), _p(hs), _p(acc_d),
                                 _p(y)), "expert_ffn")
     return y, hq, hs, acc_gu, acc_d
 
@@ -181,6 +188,8 @@ def combine(rows: np.ndarray, route_row: np.ndarray, w: np.ndarray, k: int, H: i
 def eplb_plan(token_count: np.ndarray, budget: int, D: int, primary_partition: np.ndarray,
               free_slots: np.ndarray):
     token_count = np.ascontiguousarray(token_count, np.int64)
+    primary_partition = np.ascontiguousarray(primary_partition, np.int32)
+    free_slots = np.ascontiguousarray(free_slots, np.int32)
     slices, E = token_count.shape
     P = E + budget
     out = dict(
@@ -192,8 +201,7 @@ def eplb_plan(token_count: np.ndarray, budget: int, D: int, primary_partition: n
         tail=np.full(budget + 1, np.nan, np.float64),
     )
     _check(lib().orc_eplb_plan(slices, E, _p(token_count), budget, D,
-                               _p(np.ascontiguousarray(primary_partition, np.int32)),
-                               _p(np.ascontiguousarray(free_slots, np.int32)),
+                               _p(primary_partition), _p(free_slots),
                                _p(out["replica_offsets"]), _p(out["replica_slots"]),
                                _p(out["slot_partition"]), _p(out["slot_logical"]),
                                _p(out["selected"]), _p(out["tail"])), "eplb_plan")

@@ -36,6 +36,15 @@ def _log(msg):
     print(msg, flush=True)
 
 
+@pytest.fixture(autouse=True)
+def _release_device_memory():
+    """Full-size cases hold tens of GB of static buffers: give them back after each test."""
+    yield
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 class Case:
     """Everything one workload needs, on the host (oracle) and on the device."""
 

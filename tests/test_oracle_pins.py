@@ -456,3 +456,14 @@ def test_layer_tiny_workload_end_to_end():
     assert np.array_equal(np.bincount(toks, minlength=w.T), np.full(w.T, w.k))
     assert oracle.expert_counts(r["topk_ids"], w.E).sum() == w.T * w.k
     assert np.all(np.abs(r["out"] - x) <= r["scale"][:, None] * 0.5 + 1e-6)
+
+
+def test_eplb_plan_honours_primary_partition_of_any_int_dtype():
+    """Regression: integer arrays of any dtype (converted by the wrapper) reach the
+    planner intact; primaries stay on their partitions."""
+    cnt = np.array([[50, 3, 2, 1, 1, 1]], np.int64)
+    prim = np.array([5, 4, 3, 2, 1, 0], np.int64)
+    for _ in range(20):
+        out = oracle.eplb_plan(cnt, 2, 8, prim, np.array([0, 0, 0, 0, 0, 0, 1, 1], np.int64))
+        assert out["slot_partition"][:6].tolist() == prim.tolist()
+        assert sorted(out["slot_partition"][6:].tolist()) == [6, 7]
