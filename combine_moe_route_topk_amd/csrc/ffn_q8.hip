@@ -17,9 +17,9 @@
 //   down     grouped GEMM: A = hq rows (dense, K = I), B = 128 rows of W_down;
 //            epilogue: y = bf16((f32(acc) * hs) * s_down) into the dense
 //            return rows.
-// Tiles: 128 x 128 outputs per 256-thread block (2 x 2 wavefronts of 64 x 64,
-// each 2 x 2 MFMA 32x32 blocks), K steps of 64 bytes double-buffered in LDS
-// with a 16-byte row pad.  The work list is ordered slot-major, then groups of
+// Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
+// each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes, loads two steps ahead,
+// double-buffered LDS with a 16-byte row pad.  The work list is ordered slot-major, then groups of
 // kGroupM m-tiles, then n-tiles, then m inside the group, and blocks are
 // remapped so that each XCD walks one contiguous stretch of it: the m-tiles of
 // a group share every weight tile in that XCD's L2.
@@ -31,7 +31,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row (pad breaks bank aliasing)
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
@@ -91,10 +91,18 @@ __device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t 
 }
 
 // ------------------------------------------------------------ the GEMM ---
-// MODE GATEUP: A rows gathered from the dispatch buffer, K = H, N tile = 64 gate
-//              + 64 up columns, epilogue SwiGLU -> h, partial row maxima.
-// MODE DOWN:   A rows = hq (dense), K = I, N tile = 128 output channels,
-//              epilogue -> bf16 return rows.
+// MODE GATEUP: A rows gathered from the dispatch buffer, K = H; the 256-wide N
+//              tile is 128 gate columns followed by the 128 matching up columns;
+//              epilogue: SwiGLU -> h (fp32) and per-(row, n-tile) max |h|.
+// MODE DOWN:   A rows = hq (dense), K = I; N tile = 256 output channels;
+//              epilogue: bf16 return rows.
+// Block tile 128 x 256, four wavefronts side by side along N, each owning all
+// 128 rows x 64 columns (4 x 2 MFMA 32x32 blocks, 128 accumulators): the four
+// waves share every A fragment read from LDS, which keeps LDS reads at 6 KB per
+// 32-wide K sub-step per wave.  Global loads run two K steps ahead through two
+// register sets while the current step feeds the MFMAs from LDS; LDS is
+// double-buffered, one barrier per K step; two blocks per CU overlap each
+// other's waits.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_count,
@@ -104,13 +112,16 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const float *__restrict__ wscale, int P, int E, int H, int I, int64_t nrows,
     float *__restrict__ h_out, float *__restrict__ pmax, uint16_t *__restrict__ ret,
     int32_t *__restrict__ acc_dbg) {
+  constexpr int A_CH = BM * BK / 16 / 256;  // 16-byte A chunks per thread per K step
+  constexpr int B_CH = BN * BK / 16 / 256;  // 16-byte B chunks per thread per K step
+  constexpr int MB = BM / 32, NB = 2;       // MFMA blocks per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * LDS_STRIDE];
   __shared__ float row_scale[BM];
-  __shared__ float row_max[2][BM];
+  __shared__ float row_max[4][BM];
 
   const int K = MODE == GATEUP ? H : I;
-  const int NT = MODE == GATEUP ? I / 64 : (H + BN - 1) / BN;
+  const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
   Tile tl;
   if (!decode_tile(tiles, slot_count, P, NT, tl)) return;
   const int e = slot_logical[tl.p];
@@ -120,7 +131,6 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   const int rows_here = min(BM, cnt - tl.m * BM);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
   // per-row scale of this tile (activation scale s_x, or hs)
   if (tid < BM) {
@@ -137,105 +147,130 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     row_scale[tid] = sc;
   }
 
-  // global -> LDS assignment: 2 x 16 B of A and 2 x 16 B of B per thread per K step
-  const uint8_t *a_src[2];
-  const uint8_t *b_src[2];
-  int ld_row[2], ld_col[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + i * 256;
-    ld_row[i] = idx >> 2;
-    ld_col[i] = (idx & 3) * 16;
-    const int r = ld_row[i];
-    const int64_t rr = row0 + r;
-    a_src[i] = nullptr;
-    if (r < rows_here && rr < nrows) {
-      if (MODE == GATEUP) {
-        const int32_t dr = slot_rows[rr];
-        if (dr >= 0) a_src[i] = disp_buf + (int64_t)dr * msg + ld_col[i];
-      } else {
-        a_src[i] = (const uint8_t *)hq + rr * I + ld_col[i];
-      }
-    }
-    b_src[i] = nullptr;
+  // Thread tid loads 16-byte chunk (tid & 3) of A rows tid/4 and 64 + tid/4 and
+  // of B rows tid/4 + {0, 64, 128, 192}.  Tile rows past the slot's last row,
+  // and weight rows past I or H, load a valid stand-in row instead: they only
+  // feed accumulators of rows or columns the epilogue never stores, so no load
+  // needs a mask or a branch.  (Named registers, not arrays: the staging must
+  // stay in VGPRs.)
+  static_assert(A_CH == 2 && B_CH == 4, "staging below is written for a 128 x 256 x 64 tile");
+  const int lr0 = tid >> 2, chunk = (tid & 3) * 16;
+  auto a_row_ptr = [&](int r) -> const uint8_t * {
+    r = min(r, rows_here - 1);
+    const int64_t rr = min(row0 + r, nrows - 1);
     if (MODE == GATEUP) {
-      const int wrow = r < 64 ? tl.n * 64 + r : I + tl.n * 64 + (r - 64);
-      b_src[i] = (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + ld_col[i];
-    } else {
-      const int wrow = tl.n * BN + r;
-      if (wrow < H) b_src[i] = (const uint8_t *)w + ((int64_t)e * H + wrow) * I + ld_col[i];
+      const int32_t dr = slot_rows[rr];
+      return disp_buf + (int64_t)(dr >= 0 ? dr : 0) * msg + chunk;
     }
-  }
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  uint4 ra[2], rb[2];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = a_src[i] ? *(const uint4 *)(a_src[i] + (int64_t)kt * BK) : zero4;
-      rb[i] = b_src[i] ? *(const uint4 *)(b_src[i] + (int64_t)kt * BK) : zero4;
-    }
+    return (const uint8_t *)hq + rr * I + chunk;
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(uint4 *)(&lds_a[buf][ld_row[i] * LDS_STRIDE + ld_col[i]]) = ra[i];
-      *(uint4 *)(&lds_b[buf][ld_row[i] * LDS_STRIDE + ld_col[i]]) = rb[i];
+  auto b_row_ptr = [&](int r) -> const uint8_t * {
+    if (MODE == GATEUP) {
+      const int n = min(tl.n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);  // gate / up pair index
+      const int wrow = r < BN / 2 ? n : I + n;
+      return (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + chunk;
     }
+    const int wrow = min(tl.n * BN + r, H - 1);
+    return (const uint8_t *)w + ((int64_t)e * H + wrow) * I + chunk;
   };
+  const uint8_t *pa0 = a_row_ptr(lr0), *pa1 = a_row_ptr(lr0 + 64);
+  const uint8_t *pb0 = b_row_ptr(lr0), *pb1 = b_row_ptr(lr0 + 64);
+  const uint8_t *pb2 = b_row_ptr(lr0 + 128), *pb3 = b_row_ptr(lr0 + 192);
+  const int dst0 = lr0 * LDS_STRIDE + chunk;  // LDS offset of row lr0; rows + 64 follow
+  constexpr int D64 = 64 * LDS_STRIDE;
+  // two K steps in flight between global memory and LDS: register sets 0 and 1
+  uint4 ra0_0, ra1_0, rb0_0, rb1_0, rb2_0, rb3_0;
+  uint4 ra0_1, ra1_1, rb0_1, rb1_1, rb2_1, rb3_1;
+#define MOE_GLOAD(S, kstep)                                    \
+  do {                                                         \
+    const int64_t off_ = (int64_t)(kstep) * BK;                \
+    ra0_##S = *(const uint4 *)(pa0 + off_);                    \
+    ra1_##S = *(const uint4 *)(pa1 + off_);                    \
+    rb0_##S = *(const uint4 *)(pb0 + off_);                    \
+    rb1_##S = *(const uint4 *)(pb1 + off_);                    \
+    rb2_##S = *(const uint4 *)(pb2 + off_);                    \
+    rb3_##S = *(const uint4 *)(pb3 + off_);                    \
+    __builtin_amdgcn_sched_barrier(0); /* issue before the MFMAs */ \
+  } while (0)
+#define MOE_LSTORE(S, buf)                                     \
+  do {                                                         \
+    *(uint4 *)(&lds_a[buf][dst0]) = ra0_##S;                   \
+    *(uint4 *)(&lds_a[buf][dst0 + D64]) = ra1_##S;             \
+    *(uint4 *)(&lds_b[buf][dst0]) = rb0_##S;                   \
+    *(uint4 *)(&lds_b[buf][dst0 + D64]) = rb1_##S;             \
+    *(uint4 *)(&lds_b[buf][dst0 + 2 * D64]) = rb2_##S;         \
+    *(uint4 *)(&lds_b[buf][dst0 + 3 * D64]) = rb3_##S;         \
+  } while (0)
 
-  // B-tile row offsets of this wave's two 32-column blocks
-  const int nbo0 = MODE == GATEUP ? wn * 32 : wn * 64;
-  const int nbo1 = MODE == GATEUP ? 64 + wn * 32 : wn * 64 + 32;
+  // B-tile rows of this wave's two 32-column blocks
+  const int nbo0 = MODE == GATEUP ? wave * 32 : wave * 64;
+  const int nbo1 = MODE == GATEUP ? BN / 2 + wave * 32 : wave * 64 + 32;
 
-  v16i acc[2][2];
+  v16i acc[MB][NB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
   const int KT = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  // one K step of MFMAs from LDS buffer `buf`
+  auto mfma_step = [&](int buf) {
+    const uint8_t *la = lds_a[buf];
+    const uint8_t *lb = lds_b[buf];
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int koff = ks * 32 + (lane >> 5) * 16;
-      v4i af[2], bf[2];
+      const v4i bf0 = *(const v4i *)(lb + (nbo0 + (lane & 31)) * LDS_STRIDE + koff);
+      const v4i bf1 = *(const v4i *)(lb + (nbo1 + (lane & 31)) * LDS_STRIDE + koff);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[mb] = *(const v4i *)(&lds_a[buf][(wm * 64 + mb * 32 + (lane & 31)) * LDS_STRIDE + koff]);
-      bf[0] = *(const v4i *)(&lds_b[buf][(nbo0 + (lane & 31)) * LDS_STRIDE + koff]);
-      bf[1] = *(const v4i *)(&lds_b[buf][(nbo1 + (lane & 31)) * LDS_STRIDE + koff]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) {
+        const v4i af = *(const v4i *)(la + (mb * 32 + (lane & 31)) * LDS_STRIDE + koff);
+        acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mb][1], 0, 0, 0);
+      }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+  };
+  // Pipeline, two K steps per trip: while step kt runs from LDS buffer 0, step
+  // kt + 1 waits in register set 1 and step kt + 2 is loading into set 0.  Loads
+  // past the last step re-read the last step (clamped), so no load is
+  // conditional and the wait counts stay exact.
+  MOE_GLOAD(0, 0);
+  MOE_GLOAD(1, min(1, KT - 1));
+  MOE_LSTORE(0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    MOE_GLOAD(0, min(kt + 2, KT - 1));
+    mfma_step(0);
+    MOE_LSTORE(1, 1);
+    __syncthreads();
+    MOE_GLOAD(1, min(kt + 3, KT - 1));
+    mfma_step(1);
+    MOE_LSTORE(0, 0);
     __syncthreads();
   }
+  if (kt < KT) mfma_step(0);  // odd step count: the last step sits in buffer 0
+#undef MOE_GLOAD
+#undef MOE_LSTORE
 
   // ------------------------------------------------------------ epilogue ---
-  // acc[mb][nb][r] holds output row wm*64 + mb*32 + 8*(r/4) + 4*(lane/32) + r%4,
+  // acc[mb][nb][r] holds tile row mb*32 + 8*(r/4) + 4*(lane/32) + r%4 and
   // column (lane % 32) of the wave's nb-th 32-column block.
   const int col = lane & 31, half = lane >> 5;
   if (MODE == GATEUP) {
-    const int n = tl.n * 64 + wn * 32 + col;  // gate / up pair index, < I
-    const float sg = wscale[(int64_t)e * 2 * I + n];
-    const float su = wscale[(int64_t)e * 2 * I + I + n];
+    const int n = tl.n * (BN / 2) + wave * 32 + col;  // gate / up pair index
+    const bool nok = n < I;
+    const float sg = nok ? wscale[(int64_t)e * 2 * I + n] : 0.0f;
+    const float su = nok ? wscale[(int64_t)e * 2 * I + I + n] : 0.0f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lr = wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         const int64_t rr = row0 + lr;
-        const bool ok = lr < rows_here && rr < nrows;
+        const bool ok = nok && lr < rows_here && rr < nrows;
         const int32_t ag = acc[mb][0][r], au = acc[mb][1][r];
         const float sx = row_scale[lr];
         const float g = ((float)ag * sx) * sg;
@@ -252,25 +287,26 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         float m = ok ? fabsf(hv) : 0.0f;
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (col == 0) row_max[wn][lr] = m;
+        if (col == 0) row_max[wave][lr] = m;
       }
     }
     __syncthreads();
     if (tid < BM) {
       const int64_t rr = row0 + tid;
       if (tid < rows_here && rr < nrows)
-        pmax[rr * (I / 64) + tl.n] = fmaxf(row_max[0][tid], row_max[1][tid]);
+        pmax[rr * NT + tl.n] =
+            fmaxf(fmaxf(row_max[0][tid], row_max[1][tid]), fmaxf(row_max[2][tid], row_max[3][tid]));
     }
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int c = tl.n * BN + wn * 64 + nb * 32 + col;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = tl.n * BN + wave * 64 + nb * 32 + col;
       const float sd = c < H ? wscale[(int64_t)e * H + c] : 0.0f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           const int64_t rr = row0 + lr;
           if (lr < rows_here && rr < nrows && c < H) {
             const int32_t a = acc[mb][nb][r];
@@ -296,7 +332,7 @@ __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restric
   const int lane = threadIdx.x & 63;
   const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rr >= nrows || rr >= slot_offset[P]) return;
-  const int NT = I / 64;
+  const int NT = (I + BN / 2 - 1) / (BN / 2);  // gate/up n-tiles of the row
   float m = 0.0f;
   for (int i = lane; i < NT; i += 64) m = fmaxf(m, pmax[rr * NT + i]);
   m = wave_max_f32(m);
@@ -389,7 +425,8 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->tiles);
   if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP>), gemm_grid(a->mt_bound, I / 64), dim3(256), 0, s,
+  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP>), gemm_grid(a->mt_bound, (I + BN / 2 - 1) / (BN / 2)),
+                     dim3(256), 0, s,
                      a->tiles, slot_count, slot_offset, slot_logical, slot_rows,
                      (const uint8_t *)disp_buf, a->msg, (const int8_t *)nullptr,
                      (const float *)nullptr, w_gateup, s_gateup, g->P, g->E, g->H, I, a->nrows,
@@ -414,7 +451,8 @@ extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot
   hipLaunchKernelGGL(ffn_requant_kernel, dim3((unsigned)((a->nrows + 3) / 4)), dim3(256), 0, s,
                      a->h, a->pmax, slot_offset, g->P, I, a->nrows, a->hq, a->hs);
   if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN>), gemm_grid(a->mt_bound, g->H / BN), dim3(256), 0, s,
+  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN>), gemm_grid(a->mt_bound, (g->H + BN - 1) / BN),
+                     dim3(256), 0, s,
                      a->tiles, slot_count, slot_offset, slot_logical, (const int32_t *)nullptr,
                      (const uint8_t *)nullptr, a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E,
                      g->H, I, a->nrows, (float *)nullptr, (float *)nullptr, ret, acc_down_dbg);
