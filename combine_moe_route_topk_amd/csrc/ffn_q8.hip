@@ -32,8 +32,21 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row (pad breaks bank aliasing)
+#define MOE_LDS __attribute__((address_space(3)))
+constexpr int LDS_STRIDE = BK;  // bytes per LDS row
+// LDS layout: 16-byte chunk c of tile row r sits at r * BK + 16 * (c ^ ((r >> 2) & 3)).
+// A 16-byte LDS access serves 16 lanes per cycle across 64 banks; the XOR
+// makes both access patterns conflict-free: the staging stores (16 lanes =
+// four rows x four chunks) and the MFMA operand reads (16 lanes = sixteen rows,
+// one chunk: rows r, r+4, r+8, r+12 would share banks without it).
 constexpr int kGroupM = 4;
+constexpr int kStages = 3;  // LDS ring depth: the DMA runs two K steps ahead
+// epilogue staging: 128 fp32 per row + 8 pad (rows 4 apart land 32 banks apart)
+constexpr int kStageStride = 128 + 8;
+// bf16 staging of the down projection: 256 bf16 per row + 32 B pad
+constexpr int kStageStrideB = 2 * 256 + 32;
+static_assert(128 * kStageStride * 4 <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
+static_assert(128 * kStageStrideB <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
 constexpr int kXcds = 8;
 
 enum Mode { GATEUP = 0, DOWN = 1 };
@@ -90,6 +103,17 @@ __device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t 
   return true;
 }
 
+// LDS byte address of a __shared__ object, and a 16-byte LDS read that the
+// compiler does not track (the caller waits with lgkmcnt before using it).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const MOE_LDS void *)p;
+}
+__device__ __forceinline__ v4i ds_read16(uint32_t addr) {
+  v4i v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 // ------------------------------------------------------------ the GEMM ---
 // MODE GATEUP: A rows gathered from the dispatch buffer, K = H; the 256-wide N
 //              tile is 128 gate columns followed by the 128 matching up columns;
@@ -103,7 +127,7 @@ __device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t 
 // register sets while the current step feeds the MFMAs from LDS; LDS is
 // double-buffered, one barrier per K step; two blocks per CU overlap each
 // other's waits.
-template <int MODE>
+template <int MODE, bool DBG>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_count,
     const int32_t *__restrict__ slot_offset, const int32_t *__restrict__ slot_logical,
@@ -112,11 +136,12 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const float *__restrict__ wscale, int P, int E, int H, int I, int64_t nrows,
     float *__restrict__ h_out, float *__restrict__ pmax, uint16_t *__restrict__ ret,
     int32_t *__restrict__ acc_dbg) {
-  constexpr int A_CH = BM * BK / 16 / 256;  // 16-byte A chunks per thread per K step
-  constexpr int B_CH = BN * BK / 16 / 256;  // 16-byte B chunks per thread per K step
   constexpr int MB = BM / 32, NB = 2;       // MFMA blocks per wave
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * LDS_STRIDE];
+  // one LDS arena: the K-step ring (A stages, then B stages) during the main
+  // loop, then the output staging of the epilogue
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (BM + BN) * LDS_STRIDE];
+  auto lds_a = [&](int st) { return lds + st * BM * LDS_STRIDE; };
+  auto lds_b = [&](int st) { return lds + kStages * BM * LDS_STRIDE + st * BN * LDS_STRIDE; };
   __shared__ float row_scale[BM];
   __shared__ float row_max[4][BM];
 
@@ -147,60 +172,50 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     row_scale[tid] = sc;
   }
 
-  // Thread tid loads 16-byte chunk (tid & 3) of A rows tid/4 and 64 + tid/4 and
-  // of B rows tid/4 + {0, 64, 128, 192}.  Tile rows past the slot's last row,
-  // and weight rows past I or H, load a valid stand-in row instead: they only
-  // feed accumulators of rows or columns the epilogue never stores, so no load
-  // needs a mask or a branch.  (Named registers, not arrays: the staging must
-  // stay in VGPRs.)
-  static_assert(A_CH == 2 && B_CH == 4, "staging below is written for a 128 x 256 x 64 tile");
-  const int lr0 = tid >> 2, chunk = (tid & 3) * 16;
+  // Global -> LDS by DMA (global_load_lds_dwordx4): each wavefront instruction
+  // fills one 1 KB LDS chunk = 16 tile rows x 64 bytes, lane i landing at
+  // chunk + 16 i.  Wave w fills A chunks 2w, 2w + 1 and B chunks 4w .. 4w + 3.
+  // Lane i covers row 16 q + i / 4 of chunk q and picks the source chunk
+  // (i & 3) ^ ((row >> 2) & 3), which produces the swizzled layout above.
+  // Tile rows past the slot's last row, and weight rows past I or H, read a
+  // valid stand-in row instead: they only feed accumulators of rows or
+  // columns that the epilogue never stores.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lrow = lane >> 2;
   auto a_row_ptr = [&](int r) -> const uint8_t * {
+    const int c = ((lane & 3) ^ ((r >> 2) & 3)) * 16;
     r = min(r, rows_here - 1);
     const int64_t rr = min(row0 + r, nrows - 1);
     if (MODE == GATEUP) {
       const int32_t dr = slot_rows[rr];
-      return disp_buf + (int64_t)(dr >= 0 ? dr : 0) * msg + chunk;
+      return disp_buf + (int64_t)(dr >= 0 ? dr : 0) * msg + c;
     }
-    return (const uint8_t *)hq + rr * I + chunk;
+    return (const uint8_t *)hq + rr * I + c;
   };
   auto b_row_ptr = [&](int r) -> const uint8_t * {
+    const int c = ((lane & 3) ^ ((r >> 2) & 3)) * 16;
     if (MODE == GATEUP) {
       const int n = min(tl.n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);  // gate / up pair index
       const int wrow = r < BN / 2 ? n : I + n;
-      return (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + chunk;
+      return (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + c;
     }
     const int wrow = min(tl.n * BN + r, H - 1);
-    return (const uint8_t *)w + ((int64_t)e * H + wrow) * I + chunk;
+    return (const uint8_t *)w + ((int64_t)e * H + wrow) * I + c;
   };
-  const uint8_t *pa0 = a_row_ptr(lr0), *pa1 = a_row_ptr(lr0 + 64);
-  const uint8_t *pb0 = b_row_ptr(lr0), *pb1 = b_row_ptr(lr0 + 64);
-  const uint8_t *pb2 = b_row_ptr(lr0 + 128), *pb3 = b_row_ptr(lr0 + 192);
-  const int dst0 = lr0 * LDS_STRIDE + chunk;  // LDS offset of row lr0; rows + 64 follow
-  constexpr int D64 = 64 * LDS_STRIDE;
-  // two K steps in flight between global memory and LDS: register sets 0 and 1
-  uint4 ra0_0, ra1_0, rb0_0, rb1_0, rb2_0, rb3_0;
-  uint4 ra0_1, ra1_1, rb0_1, rb1_1, rb2_1, rb3_1;
-#define MOE_GLOAD(S, kstep)                                    \
-  do {                                                         \
-    const int64_t off_ = (int64_t)(kstep) * BK;                \
-    ra0_##S = *(const uint4 *)(pa0 + off_);                    \
-    ra1_##S = *(const uint4 *)(pa1 + off_);                    \
-    rb0_##S = *(const uint4 *)(pb0 + off_);                    \
-    rb1_##S = *(const uint4 *)(pb1 + off_);                    \
-    rb2_##S = *(const uint4 *)(pb2 + off_);                    \
-    rb3_##S = *(const uint4 *)(pb3 + off_);                    \
-    __builtin_amdgcn_sched_barrier(0); /* issue before the MFMAs */ \
-  } while (0)
-#define MOE_LSTORE(S, buf)                                     \
-  do {                                                         \
-    *(uint4 *)(&lds_a[buf][dst0]) = ra0_##S;                   \
-    *(uint4 *)(&lds_a[buf][dst0 + D64]) = ra1_##S;             \
-    *(uint4 *)(&lds_b[buf][dst0]) = rb0_##S;                   \
-    *(uint4 *)(&lds_b[buf][dst0 + D64]) = rb1_##S;             \
-    *(uint4 *)(&lds_b[buf][dst0 + 2 * D64]) = rb2_##S;         \
-    *(uint4 *)(&lds_b[buf][dst0 + 3 * D64]) = rb3_##S;         \
-  } while (0)
+  const uint8_t *pa0 = a_row_ptr(16 * (2 * wv) + lrow), *pa1 = a_row_ptr(16 * (2 * wv + 1) + lrow);
+  const uint8_t *pb0 = b_row_ptr(16 * (4 * wv) + lrow), *pb1 = b_row_ptr(16 * (4 * wv + 1) + lrow);
+  const uint8_t *pb2 = b_row_ptr(16 * (4 * wv + 2) + lrow), *pb3 = b_row_ptr(16 * (4 * wv + 3) + lrow);
+  auto dma = [&](int kstep, int buf) {
+    const int64_t off = (int64_t)kstep * BK;
+    uint8_t *la = lds_a(buf) + 2 * wv * 1024;
+    uint8_t *lb = lds_b(buf) + 4 * wv * 1024;
+    __builtin_amdgcn_global_load_lds(pa0 + off, (MOE_LDS void *)(la), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pa1 + off, (MOE_LDS void *)(la + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb0 + off, (MOE_LDS void *)(lb), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb1 + off, (MOE_LDS void *)(lb + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb2 + off, (MOE_LDS void *)(lb + 2048), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb3 + off, (MOE_LDS void *)(lb + 3072), 16, 0, 0);
+  };
 
   // B-tile rows of this wave's two 32-column blocks
   const int nbo0 = MODE == GATEUP ? wave * 32 : wave * 64;
@@ -215,50 +230,64 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
   const int KT = K / BK;
-  // one K step of MFMAs from LDS buffer `buf`
-  auto mfma_step = [&](int buf) {
-    const uint8_t *la = lds_a[buf];
-    const uint8_t *lb = lds_b[buf];
+  const int mb_live = (rows_here + 31) / 32;
+  // this lane's swizzled 16-byte chunk of each 32-wide K sub-step (row blocks
+  // start at multiples of 32, so the swizzle depends on the lane only)
+  const int koff0 = ((0 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
+  const int koff1 = ((2 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
+  // Per K step: every wave waits until its own DMA of this step has landed
+  // (the DMA of the next step may still be in flight) and meets the others at
+  // the barrier, so the step's LDS stage is complete and the stage read one
+  // step ago is free; it reads all of the step's fragments, starts the DMA
+  // two steps ahead into that free stage, then runs the 16 MFMAs.
+  dma(0, 0);
+  if (KT > 1) dma(1, 1);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt % kStages;
+    if (kt + 1 < KT)
+      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): all but the next step's 6 DMAs
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    // fragment reads as raw ds_read_b128: the compiler's wait-count pass would
+    // otherwise order them after every DMA in flight (vmcnt(0)), undoing the
+    // ring; the explicit lgkmcnt(0) below makes the results safe to use.
+    const uint32_t la = lds_addr(lds_a(cur)) + (lane & 31) * LDS_STRIDE;
+    const uint32_t lb = lds_addr(lds_b(cur)) + (lane & 31) * LDS_STRIDE;
+    v4i bf[2][2], af[2][MB];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int koff = ks * 32 + (lane >> 5) * 16;
-      const v4i bf0 = *(const v4i *)(lb + (nbo0 + (lane & 31)) * LDS_STRIDE + koff);
-      const v4i bf1 = *(const v4i *)(lb + (nbo1 + (lane & 31)) * LDS_STRIDE + koff);
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t koff = ks ? koff1 : koff0;
+      bf[ks][0] = ds_read16(lb + nbo0 * LDS_STRIDE + koff);
+      bf[ks][1] = ds_read16(lb + nbo1 * LDS_STRIDE + koff);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[ks][mb] = ds_read16(la + mb * 32 * LDS_STRIDE + koff);
+    }
+    if (kt + 2 < KT) dma(kt + 2, (kt + 2) % kStages);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragments are in registers
+    __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMAs
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const v4i af = *(const v4i *)(la + (mb * 32 + (lane & 31)) * LDS_STRIDE + koff);
-        acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mb][1], 0, 0, 0);
+        if (mb >= mb_live) break;  // 32-row blocks past the slot's rows: nothing to compute
+        acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
       }
     }
-  };
-  // Pipeline, two K steps per trip: while step kt runs from LDS buffer 0, step
-  // kt + 1 waits in register set 1 and step kt + 2 is loading into set 0.  Loads
-  // past the last step re-read the last step (clamped), so no load is
-  // conditional and the wait counts stay exact.
-  MOE_GLOAD(0, 0);
-  MOE_GLOAD(1, min(1, KT - 1));
-  MOE_LSTORE(0, 0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    MOE_GLOAD(0, min(kt + 2, KT - 1));
-    mfma_step(0);
-    MOE_LSTORE(1, 1);
-    __syncthreads();
-    MOE_GLOAD(1, min(kt + 3, KT - 1));
-    mfma_step(1);
-    MOE_LSTORE(0, 0);
-    __syncthreads();
   }
-  if (kt < KT) mfma_step(0);  // odd step count: the last step sits in buffer 0
-#undef MOE_GLOAD
-#undef MOE_LSTORE
+  __syncthreads();
+
 
   // ------------------------------------------------------------ epilogue ---
   // acc[mb][nb][r] holds tile row mb*32 + 8*(r/4) + 4*(lane/32) + r%4 and
-  // column (lane % 32) of the wave's nb-th 32-column block.
+  // column (lane % 32) of the wave's nb-th 32-column block.  Results go through
+  // an fp32 LDS staging tile [128 rows][128 columns] (row stride kStageStride,
+  // padded so the two lane halves hit different banks) and leave as 16-byte
+  // vector stores.
   const int col = lane & 31, half = lane >> 5;
+  float *stg = (float *)lds;
+  auto stage_put = [&](int lr, int sc, float v) { stg[lr * kStageStride + sc] = v; };
   if (MODE == GATEUP) {
     const int n = tl.n * (BN / 2) + wave * 32 + col;  // gate / up pair index
     const bool nok = n < I;
@@ -277,12 +306,10 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         const float u = ((float)au * sx) * su;
         const float ex = (float)exp(-(double)g);
         const float hv = (g / (1.0f + ex)) * u;
-        if (ok) {
-          h_out[rr * I + n] = hv;
-          if (acc_dbg) {
-            acc_dbg[rr * 2 * I + n] = ag;
-            acc_dbg[rr * 2 * I + I + n] = au;
-          }
+        stage_put(lr, wave * 32 + col, hv);
+        if (DBG && ok) {
+          acc_dbg[rr * 2 * I + n] = ag;
+          acc_dbg[rr * 2 * I + I + n] = au;
         }
         float m = ok ? fabsf(hv) : 0.0f;
 #pragma unroll
@@ -297,25 +324,47 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         pmax[rr * NT + tl.n] =
             fmaxf(fmaxf(row_max[0][tid], row_max[1][tid]), fmaxf(row_max[2][tid], row_max[3][tid]));
     }
+    // 128 rows x 128 fp32 = 4096 chunks of 4 values
+    const int n0 = tl.n * (BN / 2);
+#pragma unroll 4
+    for (int q = tid; q < BM * (BN / 2) / 4; q += 256) {
+      const int lr = q >> 5, c4 = (q & 31) * 4;
+      const int64_t rr = row0 + lr;
+      if (lr < rows_here && rr < nrows && n0 + c4 < I)
+        *(float4 *)(h_out + rr * I + n0 + c4) = *(const float4 *)(stg + lr * kStageStride + c4);
+    }
   } else {
+    // bf16 staging [128 rows][256 columns] (row stride kStageStrideB bytes),
+    // converted before staging, so the stored bits are the same
+    const int n0 = tl.n * BN;
+    uint16_t *stb = (uint16_t *)lds;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int c = tl.n * BN + wave * 64 + nb * 32 + col;
+      const int sc = wave * 64 + nb * 32 + col;  // tile column
+      const int c = n0 + sc;
       const float sd = c < H ? wscale[(int64_t)e * H + c] : 0.0f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int32_t a = acc[mb][nb][r];
+          stb[lr * (kStageStrideB / 2) + sc] =
+              (uint16_t)f32_to_bf16_bits(((float)a * row_scale[lr]) * sd);
           const int64_t rr = row0 + lr;
-          if (lr < rows_here && rr < nrows && c < H) {
-            const int32_t a = acc[mb][nb][r];
-            const float y = ((float)a * row_scale[lr]) * sd;
-            ret[rr * H + c] = (uint16_t)f32_to_bf16_bits(y);
-            if (acc_dbg) acc_dbg[rr * H + c] = a;
-          }
+          if (DBG && lr < rows_here && rr < nrows && c < H) acc_dbg[rr * H + c] = a;
         }
       }
+    }
+    __syncthreads();
+    // 128 rows x 256 columns = 4096 chunks of 8 bf16 -> one 16-byte store each
+#pragma unroll 4
+    for (int q = tid; q < BM * (BN / 8); q += 256) {
+      const int lr = q >> 5, c8 = (q & 31) * 8;
+      const int64_t rr = row0 + lr;
+      if (lr < rows_here && rr < nrows && n0 + c8 < H)
+        *(uint4 *)(ret + rr * H + n0 + c8) =
+            *(const uint4 *)((const uint8_t *)stb + lr * kStageStrideB + c8 * 2);
     }
   }
 }
@@ -425,12 +474,17 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->tiles);
   if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP>), gemm_grid(a->mt_bound, (I + BN / 2 - 1) / (BN / 2)),
-                     dim3(256), 0, s,
-                     a->tiles, slot_count, slot_offset, slot_logical, slot_rows,
-                     (const uint8_t *)disp_buf, a->msg, (const int8_t *)nullptr,
-                     (const float *)nullptr, w_gateup, s_gateup, g->P, g->E, g->H, I, a->nrows,
-                     a->h, a->pmax, (uint16_t *)nullptr, acc_gateup_dbg);
+  const dim3 grid = gemm_grid(a->mt_bound, (I + BN / 2 - 1) / (BN / 2));
+#define MOE_GATEUP(DBG)                                                                         \
+  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP, DBG>), grid, dim3(256), 0, s, a->tiles, slot_count, \
+                     slot_offset, slot_logical, slot_rows, (const uint8_t *)disp_buf, a->msg,      \
+                     (const int8_t *)nullptr, (const float *)nullptr, w_gateup, s_gateup, g->P,    \
+                     g->E, g->H, I, a->nrows, a->h, a->pmax, (uint16_t *)nullptr, acc_gateup_dbg)
+  if (acc_gateup_dbg)
+    MOE_GATEUP(true);
+  else
+    MOE_GATEUP(false);
+#undef MOE_GATEUP
   return launch_status();
 }
 
@@ -451,11 +505,17 @@ extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot
   hipLaunchKernelGGL(ffn_requant_kernel, dim3((unsigned)((a->nrows + 3) / 4)), dim3(256), 0, s,
                      a->h, a->pmax, slot_offset, g->P, I, a->nrows, a->hq, a->hs);
   if ((st = launch_status()) != MOE_OK) return st;
-  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN>), gemm_grid(a->mt_bound, (g->H + BN - 1) / BN),
-                     dim3(256), 0, s,
-                     a->tiles, slot_count, slot_offset, slot_logical, (const int32_t *)nullptr,
-                     (const uint8_t *)nullptr, a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E,
-                     g->H, I, a->nrows, (float *)nullptr, (float *)nullptr, ret, acc_down_dbg);
+  const dim3 grid = gemm_grid(a->mt_bound, (g->H + BN - 1) / BN);
+#define MOE_DOWN(DBG)                                                                           \
+  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN, DBG>), grid, dim3(256), 0, s, a->tiles, slot_count,   \
+                     slot_offset, slot_logical, (const int32_t *)nullptr, (const uint8_t *)nullptr, \
+                     a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E, g->H, I, a->nrows,          \
+                     (float *)nullptr, (float *)nullptr, ret, acc_down_dbg)
+  if (acc_down_dbg)
+    MOE_DOWN(true);
+  else
+    MOE_DOWN(false);
+#undef MOE_DOWN
   return launch_status();
 }
 
