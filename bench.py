@@ -28,6 +28,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
+COPY_BYTES = 1 << 30       # the calibration copy: 1 GiB read + 1 GiB written per launch
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer12288_ffn_gateup_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "combine_moe_route_topk_amd", "csrc", "ffn_q8.hip")
 
 
 def log(msg):
@@ -182,6 +185,39 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+def copy_calibration(reps=5):
+    """A plain copy of known size (1 GiB fp32 -> 1 GiB), for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) that rocprofv3 reports per dispatch."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                           "launches": reps}}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary,
+    or None if the kernel source changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != sha:
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +226,8 @@ def main():
     ap.add_argument("--workload", default="layer12288")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
@@ -201,6 +239,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = mw.WORKLOADS[args.workload]
     A = algorithmic(w)
     layer, x, lg = build_layer(w)
@@ -248,7 +289,8 @@ def main():
         "roofline": {"kernel": "ffn_gemm_kernel<GATEUP> (moe_expert_gateup_q8)",
                      "bound": "mfma", "achieved": round(gu_tops, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "ops": "int8 multiply-adds x 2",
-                     "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": None},
+                     "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
