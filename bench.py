@@ -161,7 +161,7 @@ def cpu_baseline(w, budget_s=12.0):
     n_done, ffn_s, experts = 0, 0.0, []
     spent = sum(t.values())
     n = 16
-    while ffn_s < max(2.0, budget_s - spent) and n_done < 4096:
+    while ffn_s < max(2.0, budget_s - spent) and n_done < w.T * w.k:
         e = hot if not experts else int(rng.choice(np.unique(logical)))
         sel = np.nonzero(logical == e)[0]
         sel = rng.choice(sel, min(n, len(sel)), replace=False)

@@ -11,7 +11,7 @@ namespace moe {
 // ----------------------------------------------------------- host side ---
 
 inline int64_t msg_bytes_of(const moe_geom_t &g) {
-  return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 15) / 16) * 16;
+  return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 127) / 128) * 128;
 }
 inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
 

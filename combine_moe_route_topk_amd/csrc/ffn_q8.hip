@@ -18,11 +18,12 @@
 //            epilogue: y = bf16((f32(acc) * hs) * s_down) into the dense
 //            return rows.
 // Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
-// each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes, loads two steps ahead,
-// double-buffered LDS with a 16-byte row pad.  The work list is ordered slot-major, then groups of
-// kGroupM m-tiles, then n-tiles, then m inside the group, and blocks are
-// remapped so that each XCD walks one contiguous stretch of it: the m-tiles of
-// a group share every weight tile in that XCD's L2.
+// each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes moved global -> LDS by
+// DMA into a ring of three stages, two steps ahead, XOR-swizzled rows.  The
+// work list is ordered slot-major, then groups of kGroupM m-tiles, then
+// n-tiles, then m inside the group, and blocks are remapped so that each XCD
+// walks one contiguous stretch of it: the m-tiles of a group share every
+// weight tile in that XCD's L2.
 #include "common.h"
 
 namespace moe {
@@ -39,7 +40,7 @@ constexpr int LDS_STRIDE = BK;  // bytes per LDS row
 // makes both access patterns conflict-free: the staging stores (16 lanes =
 // four rows x four chunks) and the MFMA operand reads (16 lanes = sixteen rows,
 // one chunk: rows r, r+4, r+8, r+12 would share banks without it).
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;
 constexpr int kStages = 3;  // LDS ring depth: the DMA runs two K steps ahead
 // epilogue staging: 128 fp32 per row + 8 pad (rows 4 apart land 32 banks apart)
 constexpr int kStageStride = 128 + 8;
@@ -123,10 +124,9 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 // Block tile 128 x 256, four wavefronts side by side along N, each owning all
 // 128 rows x 64 columns (4 x 2 MFMA 32x32 blocks, 128 accumulators): the four
 // waves share every A fragment read from LDS, which keeps LDS reads at 6 KB per
-// 32-wide K sub-step per wave.  Global loads run two K steps ahead through two
-// register sets while the current step feeds the MFMAs from LDS; LDS is
-// double-buffered, one barrier per K step; two blocks per CU overlap each
-// other's waits.
+// 32-wide K sub-step per wave.  The DMA of step kt + 2 is in flight while
+// step kt feeds the MFMAs from LDS; one barrier per K step; two blocks per CU
+// overlap each other's waits.
 template <int MODE, bool DBG>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_count,

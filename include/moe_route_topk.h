@@ -92,7 +92,7 @@ typedef struct moe_geom {
   int32_t Epp;       /* max slots on one destination partition                */
   int32_t S;         /* source partitions                                     */
   int32_t LB;        /* local batch of each source partition                  */
-  int32_t msg_bytes; /* dispatch message row size; 0 = H + 16 rounded to 16   */
+  int32_t msg_bytes; /* dispatch message row size; 0 = H + 16 rounded to 128 */
   int32_t relays;    /* two-hop relay partitions (A2E/E2A trampoline); 0 = off */
   int32_t reserved;  /* must be 0                                             */
 } moe_geom_t;
@@ -226,7 +226,7 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
  *   disp_buf   as written by moe_dispatch_q8 (16B)
  *   w_gateup   [E][2I][H] int8 (rows 0..I-1 gate, I..2I-1 up), 16B;  s_gateup [E][2I] fp32
  *   w_down     [E][H][I] int8, 16B;  s_down [E][H] fp32
- *   I          multiple of 64, <= 16384
+ *   I          multiple of 64, <= 16384 (H a multiple of 128)
  *   ret        [T*k][H] bf16, 16B
  *   acc_gateup_dbg [T*k][2I] int32 or NULL, acc_down_dbg [T*k][H] int32 or NULL:
  *              when given, the raw int32 accumulators are written too (testing)

@@ -61,7 +61,7 @@ class Workload:
 
     @property
     def msg(self) -> int:
-        return ((self.H + 16 + 15) // 16) * 16
+        return ((self.H + 16 + 127) // 128) * 128
 
     @property
     def cap(self) -> int:

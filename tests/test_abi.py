@@ -43,10 +43,10 @@ def test_plan_sizes_reproduce_printed_static_buffers():
     assert s.dispatch_bytes_per_partition == 225 * 2 ** 20
     assert s.combine_bytes_per_partition == 420 * 2 ** 20
     assert s.dispatch_bytes == 320 * 225 * 2 ** 20
-    # default message: H + 16-byte trailer
+    # default message: H codes + 16-byte trailer, padded to a 128-byte line
     g.msg_bytes = 0
     s = moe.moe_plan_sizes(g, 0)
-    assert s.msg_bytes == 7184 and s.ffn_scratch_bytes == 0
+    assert s.msg_bytes == 7296 and s.ffn_scratch_bytes == 0
 
 
 @pytest.mark.parametrize("name", list(mw.WORKLOADS))
@@ -81,10 +81,11 @@ def test_invalid_arguments_rejected_before_launch():
     assert L.moe_dispatch_q8(fake, 0, fake, fake, 1, ctypes.byref(g), fake, fake, fake, fake, fake,
                              fake, fake, None, fake, s.dispatch_scratch_bytes - 1,
                              None) == moe.MOE_ERR_CAPACITY
-    # FFN needs H % 128 == 0 and I % 64 == 0
-    assert L.moe_expert_ffn_q8(fake, fake, fake, fake, fake, fake, fake, fake, fake, 96,
-                               ctypes.byref(g), fake, None, None, fake, 1 << 30,
-                               None) == moe.MOE_ERR_UNSUPPORTED
+    # FFN needs H % 128 == 0 and I % 64 == 0 (whole 64-byte K steps)
+    for bad_i in (96, 160):
+        assert L.moe_expert_ffn_q8(fake, fake, fake, fake, fake, fake, fake, fake, fake, bad_i,
+                                   ctypes.byref(g), fake, None, None, fake, 1 << 30,
+                                   None) == moe.MOE_ERR_UNSUPPORTED
     # relay hop without relays configured
     assert L.moe_relay_returns(fake, fake, fake, fake, ctypes.byref(g), fake,
                                None) == moe.MOE_ERR_INVALID_ARG

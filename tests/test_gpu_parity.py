@@ -21,8 +21,10 @@ RAGGED = mw.Workload("ragged", T=3 * 100, H=384, E=40, P=40, k=8, D=10, Epp=4, S
                      gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
                      experts="identity", combine="q8", out_dtype="f32")
 # small expert-FFN case: skewed slots spanning several 128-row m-tiles, empty
-# slots and ragged tails; H and I span several 64-wide K steps and n-tiles
-FFN_SMALL = mw.Workload("ffn_small", T=2 * 200, H=512, E=12, P=12, k=4, D=6, Epp=2, S=2, LB=200,
+# slots and ragged tails; H and I span several 64-byte K steps, the gate/up
+# projection's last 128-pair n-tile is half full (I = 192) and so is the down
+# projection's last 256-wide n-tile (H = 384)
+FFN_SMALL = mw.Workload("ffn_small", T=2 * 400, H=384, E=12, P=12, k=4, D=6, Epp=2, S=2, LB=400,
                         gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
                         experts="swiglu", combine="bf16", out_dtype="bf16", I=192)
 # two-hop case: 4 sources, 12 destination partitions, the first 4 are relays
