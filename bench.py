@@ -119,7 +119,52 @@ def time_gpu(layer, x, lg, steps, warmup):
     total_ms = start.elapsed_time(end)
     per = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
            for i, (name, _) in enumerate(stages)}
-    return total_ms / steps, per
+    # per-step wall time on the stream: first stage start -> last stage end
+    step_ms = sorted(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(steps))
+    q = lambda f: step_ms[min(len(step_ms) - 1, int(f * len(step_ms)))]
+    dist = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+    return total_ms / steps, per, dist
+
+
+def attainable(w, reps=5):
+    """Attainable rates on this GPU, for context next to the published peaks: a
+    plain 1 GiB device copy (HBM) and the vendor library's dense INT8 GEMM
+    (torch._int_mm) with the gate/up projection's total ops, i.e. all T*k rows
+    against one expert's [2I][H] weights (one B matrix, full reuse)."""
+    import torch
+    out = {}
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    ms = best(lambda: dst.copy_(src))
+    out["copy_GBps"] = round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    M, K, N = w.T * w.k, w.H, 2 * w.I
+    try:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        wt = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda")
+        ms = best(lambda: torch._int_mm(a, wt.t()))
+        out["int8_gemm_TOPS"] = round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)
+        out["int8_gemm"] = f"torch._int_mm [{M}x{K}] x [{K}x{N}] (dense, one weight matrix)"
+        del a, wt
+    except Exception as e:  # the library path is context only
+        out["int8_gemm_TOPS"] = None
+        out["int8_gemm"] = f"unavailable: {type(e).__name__}"
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -175,8 +220,17 @@ def cpu_baseline(w, budget_s=12.0):
         n *= 2
     t["ffn"] = ffn_s / n_done * w.T * w.k
     total = sum(t.values())
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": w.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "cpu": f"{model}; {os.cpu_count()} logical CPUs visible, {threads} OpenMP threads used",
         "sample": (f"route, quantization, dispatch layout + messages and combine over all "
                    f"{w.T} tokens; expert FFN on {n_done} sampled routes of {len(experts)} "
                    f"experts (hottest first), scaled by route count to {w.T * w.k} routes"),
@@ -225,6 +279,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer12288")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the device-copy and library-GEMM reference rates")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
@@ -245,7 +301,7 @@ def main():
     w = mw.WORKLOADS[args.workload]
     A = algorithmic(w)
     layer, x, lg = build_layer(w)
-    ms, per = time_gpu(layer, x, lg, args.steps, args.warmup)
+    ms, per, dist = time_gpu(layer, x, lg, args.steps, args.warmup)
     log(f"[bench] {ms:.3f} ms/step " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per.items()))
 
     dc_bytes = A["dispatch_bytes"] + A["combine_bytes"]
@@ -283,6 +339,7 @@ def main():
                    "sources": f"{w.S}x{w.LB}", "partitions": f"{w.D}x{w.Epp}",
                    "routing": "sigmoid(bf16 logit + log-Zipf(1.1) bias)",
                    "parallelism": "one GPU, virtual partitions"},
+        "step_ms": {k: round(v, 4) for k, v in dist.items()},
         "dispatch_combine": {"GBps": round(dc_gbs, 1), "frac_hbm_peak": round(dc_gbs / HBM_PEAK_GBS, 4),
                              "bytes": dc_bytes, "us": round(dc_ms * 1e3, 2)},
         "stages": stages,
@@ -292,6 +349,13 @@ def main():
                      "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
     }
+    if not args.no_attainable:
+        log("[bench] attainable rates: device copy, library INT8 GEMM")
+        att = attainable(w)
+        result["attainable"] = att
+        if att.get("int8_gemm_TOPS"):
+            result["roofline"]["frac_of_attainable"] = round(gu_tops / att["int8_gemm_TOPS"], 4)
+        result["dispatch_combine"]["frac_of_copy"] = round(dc_gbs / att["copy_GBps"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -4,8 +4,8 @@
 //  CMI EP320 FusedCombine (all k contributions present, dequantize, weight by
 //  the gate)]
 //
-// One wavefront per token.  The k row gathers of an element group are issued
-// together (k x 16 B per lane in flight), then summed in fp32 in ascending
+// One wavefront per token.  The k row gathers of two element groups are issued
+// together (2k x 16 B per lane in flight), then summed in fp32 in ascending
 // route order with separate multiply and add (no FMA contraction), so the
 // result is the same bits as the plain loop on the CPU.
 #include "common.h"
@@ -39,47 +39,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
     base[j] = (j < k && r >= 0) ? src + r * row_bytes : nullptr;
   }
   constexpr int EPL = Q8 ? 16 : 8;  // elements per lane per 16-byte load
+  constexpr int U = 2;              // element groups whose gathers are in flight together
   const int iters = (H + 64 * EPL - 1) / (64 * EPL);
-  for (int i = 0; i < iters; ++i) {
-    const int e0 = (i * 64 + lane) * EPL;
-    if (e0 >= H) break;
-    uint4 v[KMAX];
+  for (int i0 = 0; i0 < iters; i0 += U) {
+    uint4 v[U][KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (base[j]) v[j] = *(const uint4 *)(base[j] + (Q8 ? e0 : 2 * e0));
-    float acc[EPL];
+    for (int u = 0; u < U; ++u) {
+      const int e0 = ((i0 + u) * 64 + lane) * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (!base[j]) continue;
-      const uint32_t *wd = (const uint32_t *)&v[j];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x;
-        if (Q8) {
-          const int8_t q = (int8_t)((wd[e >> 2] >> (8 * (e & 3))) & 0xffu);
-          x = (float)q * sc[j];
-        } else {
-          x = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        }
-        const float prod = w[j] * x;
-        acc[e] = acc[e] + prod;
-      }
+      for (int j = 0; j < KMAX; ++j)
+        if (base[j] && e0 < H) v[u][j] = *(const uint4 *)(base[j] + (Q8 ? e0 : 2 * e0));
     }
-    if (OUT_BF16) {
-      uint32_t pk[EPL / 2];
 #pragma unroll
-      for (int e = 0; e < EPL / 2; ++e)
-        pk[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
-      uint4 *dst = (uint4 *)((uint16_t *)out + t * H + e0);
+    for (int u = 0; u < U; ++u) {
+      const int e0 = ((i0 + u) * 64 + lane) * EPL;
+      if (e0 >= H) break;
+      float acc[EPL];
 #pragma unroll
-      for (int q = 0; q < EPL / 8; ++q) dst[q] = make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
-    } else {
-      float4 *dst = (float4 *)((float *)out + t * H + e0);
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 #pragma unroll
-      for (int q = 0; q < EPL / 4; ++q)
-        dst[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      for (int j = 0; j < KMAX; ++j) {
+        if (!base[j]) continue;
+        const uint32_t *wd = (const uint32_t *)&v[u][j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float x;
+          if (Q8) {
+            const int8_t q = (int8_t)((wd[e >> 2] >> (8 * (e & 3))) & 0xffu);
+            x = (float)q * sc[j];
+          } else {
+            x = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          }
+          const float prod = w[j] * x;
+          acc[e] = acc[e] + prod;
+        }
+      }
+      if (OUT_BF16) {
+        uint32_t pk[EPL / 2];
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e)
+          pk[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+        uint4 *dst = (uint4 *)((uint16_t *)out + t * H + e0);
+#pragma unroll
+        for (int q = 0; q < EPL / 8; ++q)
+          dst[q] = make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+      } else {
+        float4 *dst = (float4 *)((float *)out + t * H + e0);
+#pragma unroll
+        for (int q = 0; q < EPL / 4; ++q)
+          dst[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      }
     }
   }
 }

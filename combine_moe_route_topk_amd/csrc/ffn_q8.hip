@@ -371,44 +371,57 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 
 // ---------------------------------------------------------------- requant ---
 // One wavefront per row: amax = max of the gate-up partial maxima, then the
-// token-wise INT8 rule (IEEE divide, round half to even, clamp +-127).
+// token-wise INT8 rule (IEEE divide, round half to even, clamp +-127).  Lane l
+// holds the float4 groups q * 64 + l of the row, so every load instruction
+// reads 1 KB of consecutive bytes and every store writes 256; all of a row's
+// loads are issued before the reduction that needs the maxima.
+constexpr int kRequantMaxI = 2048;  // the register copy of a row; longer rows take a second pass
 __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restrict__ h,
                                                           const float *__restrict__ pmax,
                                                           const int32_t *__restrict__ slot_offset,
                                                           int P, int I, int64_t nrows,
                                                           int8_t *__restrict__ hq,
                                                           float *__restrict__ hs) {
+  constexpr int G = kRequantMaxI / 256;  // float4 groups per lane
   const int lane = threadIdx.x & 63;
   const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rr >= nrows || rr >= slot_offset[P]) return;
   const int NT = (I + BN / 2 - 1) / (BN / 2);  // gate/up n-tiles of the row
+  const int n4 = I / 4;                         // float4 groups of the row
+  const float4 *src = (const float4 *)(h + rr * I);
+  float4 v[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int c = q * 64 + lane;
+    if (c < n4) v[q] = src[c];
+  }
   float m = 0.0f;
   for (int i = lane; i < NT; i += 64) m = fmaxf(m, pmax[rr * NT + i]);
   m = wave_max_f32(m);
   const float s = m / 127.0f;
   if (lane == 0) hs[rr] = s;
-  for (int e0 = lane * 16; e0 < I; e0 += 64 * 16) {
-    const float4 *src = (const float4 *)(h + rr * I + e0);
-    uint32_t pk[4];
+  auto code4 = [&](float4 x) -> uint32_t {
+    const float f[4] = {x.x, x.y, x.z, x.w};
+    uint32_t word = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = src[q];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      uint32_t word = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int code = 0;
-        if (s != 0.0f) {
-          float y = rintf(f[r] / s);
-          y = fminf(fmaxf(y, -127.0f), 127.0f);
-          code = (int)y;
-        }
-        word |= ((uint32_t)code & 0xffu) << (8 * r);
+    for (int r = 0; r < 4; ++r) {
+      int code = 0;
+      if (s != 0.0f) {
+        float y = rintf(f[r] / s);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        code = (int)y;
       }
-      pk[q] = word;
+      word |= ((uint32_t)code & 0xffu) << (8 * r);
     }
-    *(uint4 *)(hq + rr * I + e0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    return word;
+  };
+  uint32_t *dst = (uint32_t *)(hq + rr * I);
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int c = q * 64 + lane;
+    if (c < n4) dst[c] = code4(v[q]);
   }
+  for (int c = kRequantMaxI / 4 + lane; c < n4; c += 64) dst[c] = code4(src[c]);
 }
 
 }  // namespace

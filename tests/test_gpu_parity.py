@@ -169,7 +169,9 @@ def test_dispatch_twohop_small_equals_direct():
     direct.layer.event_id = c.event_id - 1
     direct.layer.dispatch(direct.x_d)
     rows = host(c.layer.buf.disp_row).ravel()
-    assert np.array_equal(gather_rows(c.layer.buf, rows), gather_rows(direct.layer.buf, rows))
+    n = c.w.H + 16  # codes + trailer; the line padding after them is unspecified
+    assert np.array_equal(gather_rows(c.layer.buf, rows)[:, :n],
+                          gather_rows(direct.layer.buf, rows)[:, :n])
 
 
 def test_dispatch_twohop46080_full_layout_sampled_rows():
