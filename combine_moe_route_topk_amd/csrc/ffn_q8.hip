@@ -143,7 +143,6 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   auto lds_a = [&](int st) { return lds + st * BM * LDS_STRIDE; };
   auto lds_b = [&](int st) { return lds + kStages * BM * LDS_STRIDE + st * BN * LDS_STRIDE; };
   __shared__ float row_scale[BM];
-  __shared__ float row_max[4][BM];
 
   const int K = MODE == GATEUP ? H : I;
   const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
@@ -306,23 +305,29 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         const float u = ((float)au * sx) * su;
         const float ex = (float)exp(-(double)g);
         const float hv = (g / (1.0f + ex)) * u;
+        // columns past I stage 0 (g = u = 0), so the row scans below see only real h
         stage_put(lr, wave * 32 + col, hv);
         if (DBG && ok) {
           acc_dbg[rr * 2 * I + n] = ag;
           acc_dbg[rr * 2 * I + I + n] = au;
         }
-        float m = ok ? fabsf(hv) : 0.0f;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (col == 0) row_max[wave][lr] = m;
       }
     }
     __syncthreads();
+    // max |h| of each row over this n-tile: one thread per row scans the staged
+    // row (a cross-lane reduction per value costs far more)
     if (tid < BM) {
       const int64_t rr = row0 + tid;
-      if (tid < rows_here && rr < nrows)
-        pmax[rr * NT + tl.n] =
-            fmaxf(fmaxf(row_max[0][tid], row_max[1][tid]), fmaxf(row_max[2][tid], row_max[3][tid]));
+      if (tid < rows_here && rr < nrows) {
+        const float4 *rowp = (const float4 *)(stg + tid * kStageStride);
+        float m = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < BN / 2 / 4; ++c) {
+          const float4 v = rowp[c];
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        pmax[rr * NT + tl.n] = m;
+      }
     }
     // 128 rows x 128 fp32 = 4096 chunks of 4 values
     const int n0 = tl.n * (BN / 2);
