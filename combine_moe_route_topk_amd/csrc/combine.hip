@@ -7,11 +7,15 @@
 // One wavefront per token.  The k row gathers of two element groups are issued
 // together (2k x 16 B per lane in flight), then summed in fp32 in ascending
 // route order with separate multiply and add (no FMA contraction), so the
-// result is the same bits as the plain loop on the CPU.
+// result is the same bits as the plain loop on the CPU.  Every value row is
+// read exactly once, so the gathers are non-temporal loads (measured on the
+// 12288-token layer: 284 us instead of 323 us).
 #include "common.h"
 
 namespace moe {
 namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 template <bool Q8, bool OUT_BF16, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict__ src,
@@ -48,7 +52,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
       const int e0 = ((i0 + u) * 64 + lane) * EPL;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (base[j] && e0 < H) v[u][j] = *(const uint4 *)(base[j] + (Q8 ? e0 : 2 * e0));
+        if (base[j] && e0 < H) {
+          const v4u lv = __builtin_nontemporal_load((const v4u *)(base[j] + (Q8 ? e0 : 2 * e0)));
+          v[u][j] = make_uint4(lv.x, lv.y, lv.z, lv.w);
+        }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -35,7 +35,7 @@ inline int launch_status() { return hip_status(hipGetLastError()); }
 
 // Byte layout of the dispatch scratch (all offsets 256-aligned).
 struct DispatchScratch {
-  int64_t status;       // int32 device status word
+  int64_t status;       // int32 device status word, then the scan's int32 completion counter
   int64_t hist_d;       // int32 [D][NC+1]  per-chunk route counts per destination partition
   int64_t hist_p;       // int32 [P][NC+1]  per-chunk route counts per slot
   int64_t route_rank;   // int32 [T*k]    (rank in chunk for d) | (rank in chunk for p) << 16
@@ -60,12 +60,13 @@ FfnScratch ffn_scratch_layout(const moe_geom_t &g, int32_t I);
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
-// round to nearest even (finite inputs; NaN is kept a quiet NaN)
+// round to nearest even (finite inputs; infinities stay infinite, NaN is kept
+// a NaN); written without branches so that it vectorizes in epilogues
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t special = (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  return (u & 0x7f800000u) == 0x7f800000u ? special : rounded;
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {

@@ -19,17 +19,19 @@
 //               histograms in (source, chunk) order.  For d this single prefix
 //               is both the receive layout offset of source s (its value at
 //               s's first chunk) and, relative to it, the chunk's base row in
-//               region (d, s).
-//   3. finalize slot_count / slot_offset / slot_local; clears the status word.
-//   4. scatter  one wavefront per token: amax, scale, IEEE divide + RNE to
+//               region (d, s); the d blocks write meta.  The last p block
+//               writes slot_offset / slot_local; the status word is cleared.
+//   3. scatter  one wavefront per token: amax, scale, IEEE divide + RNE to
 //               int8, 16-byte stores of the k message rows and trailers.
-//   5. relay    (two-hop only) second hop: relay region rows -> final region.
+//   4. relay    (two-hop only) second hop: relay region rows -> final region.
 // No atomics decide any order: every row index is a deterministic function of
 // the routes, so the layout is bit-identical run to run.
 #include "common.h"
 
 namespace moe {
 namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -57,7 +59,7 @@ __device__ __forceinline__ int bits_for(int n) {
 __global__ __launch_bounds__(256) void dispatch_count_kernel(
     const int32_t *__restrict__ phys, const int32_t *__restrict__ slot_partition, int T, int k,
     int P, int D, int LB, int ct, int cps, int nc, int32_t *__restrict__ hist_d,
-    int32_t *__restrict__ hist_p, int32_t *__restrict__ route_rank) {
+    int32_t *__restrict__ hist_p, int32_t *__restrict__ route_rank, int32_t *__restrict__ done) {
   extern __shared__ int32_t lds[];
   int32_t *wd = lds;              // [4][D]
   int32_t *wp = lds + 4 * D;      // [4][P]
@@ -68,6 +70,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
   const int n = (int)(t1 - t0) * k;
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * (D + P); i += 256) lds[i] = 0;
+  if (c == 0 && tid == 0) *done = 0;  // completion counter of the scan kernel that follows
   __syncthreads();
 
   const int64_t gi = t0 * k + tid;
@@ -125,11 +128,23 @@ __device__ __forceinline__ int block_incl_scan_256(int v, int *sh) {
   return v + add;
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t *__restrict__ hist_d,
-                                                            int32_t *__restrict__ hist_p, int D,
-                                                            int nc) {
+// Block b < D scans hist_d row b and writes meta[b][s] = {event, prefix at
+// s's first chunk, count} for every source s; block D + p scans hist_p row p
+// and writes slot_count[p].  Scans are exclusive over the nc chunks, the total
+// goes to column nc.  The last slot block to finish (an agent-scope
+// acquire-release counter, zeroed by the count kernel) prefixes the slot
+// totals into slot_offset and writes slot_local; block 0 clears the status
+// word, so no separate finalize launch is needed.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+    int32_t *__restrict__ hist_d, int32_t *__restrict__ hist_p,
+    const int32_t *__restrict__ slot_partition, int D, int P, int S, int cps, int nc,
+    uint32_t event_id, moe_meta_t *__restrict__ meta, int32_t *__restrict__ slot_count,
+    int32_t *__restrict__ slot_offset, int32_t *__restrict__ slot_local,
+    int32_t *__restrict__ status, int32_t *__restrict__ done) {
   __shared__ int sh[4];
   __shared__ int carry_sh;
+  __shared__ int last;
+  __shared__ int part[MOE_MAX_P];
   const bool is_d = blockIdx.x < (unsigned)D;
   const int row = is_d ? blockIdx.x : blockIdx.x - D;
   int32_t *h = (is_d ? hist_d : hist_p) + (int64_t)row * (nc + 1);
@@ -145,61 +160,56 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t *__restrict_
     __syncthreads();
   }
   if (threadIdx.x == 0) h[nc] = carry;
-}
-
-// -------------------------------------------------------------- finalize ---
-// Block 0: slot_count / slot_offset (P <= 1024) / slot_local, clears the status
-// word.  Blocks 1..: meta[d][s] = {event, prefix at s's first chunk, count}.
-__global__ __launch_bounds__(1024) void dispatch_finalize_kernel(
-    const int32_t *__restrict__ hist_d, const int32_t *__restrict__ hist_p,
-    const int32_t *__restrict__ slot_partition, int D, int P, int S, int cps, int nc,
-    uint32_t event_id, moe_meta_t *__restrict__ meta, int32_t *__restrict__ slot_count,
-    int32_t *__restrict__ slot_offset, int32_t *__restrict__ slot_local,
-    int32_t *__restrict__ status) {
-  if (blockIdx.x > 0) {
-    const int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x;
-    if (i >= (int64_t)D * S) return;
-    const int d = (int)(i / S), s = (int)(i % S);
-    const int32_t *h = hist_d + (int64_t)d * (nc + 1);
-    const int a = h[s * cps], b = h[(s + 1) * cps];  // (s + 1) * cps <= nc: column nc is the total
-    moe_meta_t m;
-    m.event_id = event_id;
-    m.offset = a;
-    m.count = b - a;
-    m.reserved = 0;
-    meta[i] = m;
+  if (is_d) {
+    __syncthreads();  // the block's scanned row is visible to all its threads
+    for (int src = threadIdx.x; src < S; src += 256) {
+      const int a = h[src * cps], b = h[(src + 1) * cps];  // (src + 1) * cps <= nc
+      moe_meta_t m;
+      m.event_id = event_id;
+      m.offset = a;
+      m.count = b - a;
+      m.reserved = 0;
+      meta[(int64_t)row * S + src] = m;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
     return;
   }
-  __shared__ int sh[16];
-  __shared__ int part[MOE_MAX_P];
-  const int p = threadIdx.x, lane = p & 63, wave = p >> 6;
-  if (p < P) part[p] = slot_partition[p];
-  const int v = p < P ? hist_p[(int64_t)p * (nc + 1) + nc] : 0;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
+  if (threadIdx.x == 0) {
+    slot_count[row] = carry;
+    // release: this block's total is visible before the count goes up
+    last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == P - 1;
   }
-  if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += sh[w];
-  if (p < P) {
-    slot_count[p] = v;
-    slot_offset[p] = incl - v;
-    if (p == P - 1) slot_offset[P] = incl;
-    const int d = part[p];  // part[] is complete: the scan above passed a barrier
-    int nloc = 0;
-    for (int q = 0; q < p; ++q) nloc += part[q] == d;
-    slot_local[p] = nloc;
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every slot block's total is visible
+  int off = 0;
+  for (int base = 0; base < P; base += 256) {
+    const int q = base + threadIdx.x;
+    const int v = q < P ? hist_p[(int64_t)q * (nc + 1) + nc] : 0;
+    const int incl = block_incl_scan_256(v, sh);
+    if (q < P) slot_offset[q] = off + incl - v;
+    if (threadIdx.x == 255) carry_sh = incl;
+    __syncthreads();
+    off += carry_sh;
+    __syncthreads();
   }
-  if (p == 0) *status = 0;
+  if (threadIdx.x == 0) slot_offset[P] = off;
+  for (int q = threadIdx.x; q < P; q += 256) part[q] = slot_partition[q];
+  __syncthreads();
+  for (int q = threadIdx.x; q < P; q += 256) {
+    const int d = part[q];
+    int nloc = 0;
+    for (int r = 0; r < q; ++r) nloc += part[r] == d;
+    slot_local[q] = nloc;
+  }
 }
 
 // -------------------------------------------------------------- scatter ---
 // One wavefront per token.  Lane l, iteration i covers elements
 // [(i*64 + l)*16, +16) of the row: 32 B (bf16) or 64 B (fp32) loads and one
-// 16-byte int8 store per message copy.
+// 16-byte int8 store per message copy.  The token rows are read once: bf16
+// rows come in by non-temporal loads (non-temporal stores of the messages
+// measured slower, ordinary stores are kept).
 template <int NIT, bool BF16>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const void *__restrict__ x, const int32_t *__restrict__ phys,
@@ -257,9 +267,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int e0 = (i * 64 + lane) * 16;
     if (e0 < H) {
       if (BF16) {
-        const uint4 *src = (const uint4 *)((const uint16_t *)x + t * H + e0);
-        raw[i][0] = src[0];
-        raw[i][1] = src[1];
+        const v4u *src = (const v4u *)((const uint16_t *)x + t * H + e0);
+        const v4u a0 = __builtin_nontemporal_load(src), a1 = __builtin_nontemporal_load(src + 1);
+        raw[i][0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+        raw[i][1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
         const uint32_t *w = (const uint32_t *)&raw[i][0];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -432,16 +443,13 @@ extern "C" int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t
   const int64_t cap = cap_of(*g), msg = msg_bytes_of(*g);
 
   const size_t lds = sizeof(int32_t) * 4 * (g->D + g->P);
+  int32_t *done = status + 1;  // scan completion counter, beside the status word
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nc), dim3(256), lds, s, phys_ids, slot_partition,
-                     g->T, g->k, g->P, g->D, g->LB, ct, cps, nc, hist_d, hist_p, route_rank);
+                     g->T, g->k, g->P, g->D, g->LB, ct, cps, nc, hist_d, hist_p, route_rank, done);
   if ((st = launch_status()) != MOE_OK) return st;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(g->D + g->P), dim3(256), 0, s, hist_d, hist_p,
-                     g->D, nc);
-  if ((st = launch_status()) != MOE_OK) return st;
-  const unsigned fin_blocks = 1 + (unsigned)(((int64_t)g->D * g->S + 1023) / 1024);
-  hipLaunchKernelGGL(dispatch_finalize_kernel, dim3(fin_blocks), dim3(1024), 0, s, hist_d, hist_p,
                      slot_partition, g->D, g->P, g->S, cps, nc, event_id, meta, slot_count,
-                     slot_offset, slot_local, status);
+                     slot_offset, slot_local, status, done);
   if ((st = launch_status()) != MOE_OK) return st;
 
   const dim3 grid((unsigned)((g->T + 3) / 4));

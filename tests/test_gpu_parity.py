@@ -20,11 +20,11 @@ pytestmark = pytest.mark.gpu
 RAGGED = mw.Workload("ragged", T=3 * 100, H=384, E=40, P=40, k=8, D=10, Epp=4, S=3, LB=100,
                      gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
                      experts="identity", combine="q8", out_dtype="f32")
-# small expert-FFN case: skewed slots spanning several 128-row m-tiles, empty
-# slots and ragged tails; H and I span several 64-byte K steps, the gate/up
-# projection's last 128-pair n-tile is half full (I = 192) and so is the down
-# projection's last 256-wide n-tile (H = 384)
-FFN_SMALL = mw.Workload("ffn_small", T=2 * 400, H=384, E=12, P=12, k=4, D=6, Epp=2, S=2, LB=400,
+# small expert-FFN case: skewed slots from 1 row (less than one 32-row MFMA
+# block) to several 128-row m-tiles with ragged tails; H and I span several
+# 64-byte K steps, the gate/up projection's last 128-pair n-tile is half full
+# (I = 192) and so is the down projection's last 256-wide n-tile (H = 384)
+FFN_SMALL = mw.Workload("ffn_small", T=2 * 400, H=384, E=32, P=32, k=4, D=8, Epp=4, S=2, LB=400,
                         gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
                         experts="swiglu", combine="bf16", out_dtype="bf16", I=192)
 # two-hop case: 4 sources, 12 destination partitions, the first 4 are relays
@@ -294,6 +294,7 @@ def test_expert_ffn_parity_small():
     c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
     sc = lay["slot_count"]
     assert sc.max() > 256, "want a slot spanning three 128-row m-tiles"
+    assert 0 < sc[sc > 0].min() < 32, "want a slot smaller than one 32-row MFMA block"
     n = w.T * w.k
     acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
     acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
