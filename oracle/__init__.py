@@ -35,10 +35,12 @@ def lib():
         L.orc_dispatch_layout.argtypes = [_P, _P, _P, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P]
         L.orc_dispatch_rows.argtypes = [_P, _P, _P, _P, _P, ctypes.c_uint32, _I64, _I64, _P]
         L.orc_expert_ffn.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
-        L.orc_combine.argtypes = [_I32, _I32, _I32, _I32, _P, _I64, _I64, _P, _P, _I32, _P]
+        L.orc_combine.argtypes = [_I32, _I32, _I32, _I32, _P, _I64, _I64, _I32, _P, _P, _I32, _P]
+        L.orc_quant_blocks.argtypes = [_I32, _I32, _I32, _P, _P, _P]
         L.orc_eplb_plan.argtypes = [_I32, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]
         L.orc_static_buffer.argtypes = [_I64, _I64, _I64, _I64, _I64, _P]
-        for f in ("orc_route_topk", "orc_eplb_phys", "orc_quant_tokens", "orc_dispatch_layout",
+        for f in ("orc_route_topk", "orc_eplb_phys", "orc_quant_tokens", "orc_quant_blocks",
+                  "orc_dispatch_layout",
                   "orc_dispatch_rows", "orc_expert_ffn", "orc_combine", "orc_eplb_plan",
                   "orc_static_buffer"):
             getattr(L, f).restype = ctypes.c_int
@@ -171,18 +173,41 @@ def expert_ffn(q_rows, s_rows, wgu, sgu, wd, sd, want_acc: bool = False):
 
 
 def combine(rows: np.ndarray, route_row: np.ndarray, w: np.ndarray, k: int, H: int, mode: str,
-            out_bf16: bool, scale_offset: int = 0):
+            out_bf16: bool, scale_offset: int = 0, scale_block: int = 0):
     """mode 'q8': rows are message rows (int8 payload, fp32 scale at scale_offset);
-    mode 'bf16': rows are bf16 value rows.  route_row[t][j] indexes rows."""
+    mode 'bf16': rows are bf16 value rows; mode 'q8blocks': int8 payload with one fp32
+    scale per `scale_block` columns, stored from scale_offset.  route_row[t][j] indexes rows."""
     rows = np.ascontiguousarray(rows)
     route_row = np.ascontiguousarray(route_row, np.int32)
     w = np.ascontiguousarray(w, np.float32)
     T = route_row.shape[0]
     out = np.empty((T, H), np.uint16 if out_bf16 else np.float32)
     stride = rows.shape[1] * rows.itemsize
-    _check(lib().orc_combine(T, k, H, 0 if mode == "q8" else 1, _p(rows), stride, scale_offset,
+    m = {"q8": 0, "bf16": 1, "q8blocks": 2}[mode]
+    _check(lib().orc_combine(T, k, H, m, _p(rows), stride, scale_offset, scale_block,
                              _p(route_row), _p(w), int(out_bf16), _p(out)), "combine")
     return out
+
+
+def quant_blocks(y: np.ndarray, block: int):
+    """INT8 of bf16 rows y [n][H] (bits) with one scale per `block` columns:
+    (q [n][H] int8, scale [n][ceil(H / block)] f32)."""
+    y = np.ascontiguousarray(y, np.uint16)
+    n, H = y.shape
+    nblk = (H + block - 1) // block
+    q = np.empty((n, H), np.int8)
+    s = np.empty((n, nblk), np.float32)
+    _check(lib().orc_quant_blocks(n, H, block, _p(y), _p(q), _p(s)), "quant_blocks")
+    return q, s
+
+
+def int8_return_rows(q: np.ndarray, s: np.ndarray, row_bytes: int) -> np.ndarray:
+    """Pack INT8 return rows: H codes, then the fp32 block scales, zero padding to row_bytes."""
+    n, H = q.shape
+    rows = np.zeros((n, row_bytes), np.uint8)
+    rows[:, :H] = q.view(np.uint8)
+    rows[:, H:H + 4 * s.shape[1]] = np.ascontiguousarray(s, np.float32).view(np.uint8)
+    return rows
 
 
 def eplb_plan(token_count: np.ndarray, budget: int, D: int, primary_partition: np.ndarray,

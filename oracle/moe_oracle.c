@@ -188,6 +188,48 @@ int orc_quant_tokens(int32_t T, int32_t H, const void *x, int32_t x_bf16, int8_t
   return ORC_OK;
 }
 
+/* ------------------------------------ c6': INT8 expert returns (blocks) -- */
+/*
+ * Expert outputs quantized to INT8 before they travel back [XDS DeepSeek INT8
+ * 量化, P089: expert inputs and outputs are quantized to INT8 before
+ * cross-node transfer, with the quantization fused into the communication
+ * operators].  The pages do not fix the scale granularity of the outputs; here
+ * every row of bf16 outputs y[n][H] is cut into blocks of `block` columns (the
+ * last one may be shorter) and each block gets the c3 rule of its own:
+ *   a = max |y| over the block;  s = a / 127 (fp32 division);
+ *   q = clamp(round_half_even(y / s), -127, 127)   (fp32 division);
+ *   a == 0 gives s = 0 and q = 0.
+ * scale[r][b] is the scale of block b of row r (nblk = ceil(H / block)).
+ */
+int orc_quant_blocks(int32_t n, int32_t H, int32_t block, const uint16_t *y, int8_t *q, float *scale) {
+  if (n < 0 || H <= 0 || block <= 0 || !y || !q || !scale) return ORC_EINVAL;
+  const int32_t nblk = (H + block - 1) / block;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int32_t b = 0; b < nblk; ++b) {
+      const int32_t c0 = b * block, c1 = c0 + block < H ? c0 + block : H;
+      float amax = 0.0f;
+      for (int32_t c = c0; c < c1; ++c) {
+        float a = fabsf(orc_bf16_to_f32(y[r * H + c]));
+        if (a > amax) amax = a;
+      }
+      float sb = amax / 127.0f;
+      scale[r * nblk + b] = sb;
+      for (int32_t c = c0; c < c1; ++c) {
+        if (sb == 0.0f) {
+          q[r * H + c] = 0;
+          continue;
+        }
+        float v = rintf(orc_bf16_to_f32(y[r * H + c]) / sb);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+        q[r * H + c] = (int8_t)v;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------- c4: dispatch layout -- */
 /*
  * geom = {T, H, E, P, k, D, Epp, S, LB, msg}.
@@ -395,13 +437,16 @@ int orc_expert_ffn(int32_t n, int32_t H, int32_t I, const int8_t *q_rows, const 
  *   out[t][c] = sum_{j = 0..k-1} w[t][j] * v_j[c]   (fp32, ascending j, from 0)
  * v_j is the value row of route (t, j), found at rows + route_row[t*k+j] * row_stride:
  *   mode 0 (INT8 row): v = float(q[c]) * scale, scale = fp32 at byte scale_offset of the row;
- *   mode 1 (bf16 row): v = float(bf16[c]).
+ *   mode 1 (bf16 row): v = float(bf16[c]);
+ *   mode 2 (INT8 row with block scales, c6'): v = float(q[c]) * scale[c / scale_block],
+ *          the fp32 block scales stored from byte scale_offset of the row.
  * out is fp32 [T][H] or, with out_bf16, bf16 bits rounded to nearest even.
  */
 int orc_combine(int32_t T, int32_t k, int32_t H, int32_t mode, const void *rows, int64_t row_stride,
-                int64_t scale_offset, const int32_t *route_row, const float *w, int32_t out_bf16,
-                void *out) {
+                int64_t scale_offset, int32_t scale_block, const int32_t *route_row,
+                const float *w, int32_t out_bf16, void *out) {
   if (T < 0 || k <= 0 || H <= 0 || !rows || !route_row || !w || !out) return ORC_EINVAL;
+  if (mode < 0 || mode > 2 || (mode == 2 && scale_block <= 0)) return ORC_EINVAL;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t c = 0; c < H; ++c) {
@@ -409,9 +454,10 @@ int orc_combine(int32_t T, int32_t k, int32_t H, int32_t mode, const void *rows,
       for (int64_t j = 0; j < k; ++j) {
         const uint8_t *row = (const uint8_t *)rows + (int64_t)route_row[t * k + j] * row_stride;
         float v;
-        if (mode == 0) {
+        if (mode == 0 || mode == 2) {
           float sc;
-          memcpy(&sc, row + scale_offset, 4);
+          const int64_t so = scale_offset + (mode == 2 ? 4 * (c / scale_block) : 0);
+          memcpy(&sc, row + so, 4);
           v = (float)((const int8_t *)row)[c] * sc;
         } else {
           v = orc_bf16_to_f32(((const uint16_t *)row)[c]);

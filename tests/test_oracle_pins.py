@@ -367,6 +367,64 @@ def test_combine_against_float64_einsum_and_unit_weight():
     assert np.array_equal(one, _bf16_to_f32(vals)[rr[:, 0]])
 
 
+# ----------------------------------------- c6' INT8 returns (block scales) ---
+
+def test_quant_blocks_equal_token_rule_per_block():
+    """XDS P089 (outputs quantized to INT8 before they travel): each 256-column
+    block of a row, partial last block included, gets exactly the codes and
+    scale that the pinned token rule (c3) gives that block on its own; an
+    all-zero block has s = 0, q = 0; the block amax element maps to +-127 and
+    |y - q s| <= s (0.5 + 2^-16)."""
+    rng = np.random.default_rng(21)
+    n, H, B = 24, 640, 256  # blocks of 256, 256 and 128 columns
+    yf = rng.standard_normal((n, H)).astype(np.float32) * rng.uniform(1e-3, 1e2, (n, 1)).astype(np.float32)
+    yf[3, 256:512] = 0.0
+    y = mw.to_bf16_bits(yf)
+    q, s = oracle.quant_blocks(y, B)
+    assert s.shape == (n, 3)
+    for b in range(3):
+        c0, c1 = b * B, min(H, (b + 1) * B)
+        qt, st = oracle.quant_tokens(np.ascontiguousarray(y[:, c0:c1]), True)
+        assert np.array_equal(q[:, c0:c1], qt) and np.array_equal(s[:, b], st)
+    assert s[3, 1] == 0 and np.all(q[3, 256:512] == 0)
+    yd = _bf16_to_f32(y).astype(np.float64)
+    sb = np.repeat(s, B, axis=1)[:, :H].astype(np.float64)
+    assert np.all(np.abs(yd - q * sb) <= sb * (0.5 + 2.0 ** -16))
+    for b in range(3):
+        c0, c1 = b * B, min(H, (b + 1) * B)
+        i = np.abs(yd[:, c0:c1]).argmax(1)
+        live = s[:, b] > 0
+        assert np.all(np.abs(q[np.arange(n)[live], c0 + i[live]]) == 127)
+
+
+def test_combine_block_scales_reduce_to_row_scale_and_closed_form():
+    """Combine of INT8 rows with block scales: with one block spanning the row it
+    is the pinned single-scale INT8 mode exactly; k = 1, w = 1 gives q * s of
+    each column's block exactly; fp32 accumulation agrees with a float64 einsum
+    of the dequantized rows to fp32 rounding."""
+    rng = np.random.default_rng(22)
+    T, k, H, B = 30, 4, 320, 128
+    y = mw.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    q, sblk = oracle.quant_blocks(y, B)
+    rb = ((H + 4 * sblk.shape[1] + 15) // 16) * 16
+    rows = oracle.int8_return_rows(q, sblk, rb)
+    wts = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    rr = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    out = oracle.combine(rows, rr, wts, k, H, "q8blocks", False, scale_offset=H, scale_block=B)
+    v = q.astype(np.float64) * np.repeat(sblk, B, axis=1)[:, :H]
+    ref = np.einsum("tj,tjc->tc", wts.astype(np.float64), v[rr])
+    bound = 8 * 2.0 ** -24 * np.einsum("tj,tjc->tc", wts.astype(np.float64), np.abs(v[rr]))
+    assert np.all(np.abs(out - ref) <= bound + 1e-30)
+    one = oracle.combine(rows, rr[:, :1], np.ones((T, 1), np.float32), 1, H, "q8blocks", False,
+                         scale_offset=H, scale_block=B)
+    assert np.array_equal(one, (q.astype(np.float32) * np.repeat(sblk, B, axis=1)[:, :H])[rr[:, 0]])
+    q1, s1 = oracle.quant_blocks(y, H)
+    rows1 = oracle.int8_return_rows(q1, s1, rb)
+    a = oracle.combine(rows1, rr, wts, k, H, "q8blocks", False, scale_offset=H, scale_block=H)
+    b = oracle.combine(rows1, rr, wts, k, H, "q8", False, scale_offset=H)
+    assert np.array_equal(a, b)
+
+
 # ------------------------------------------------------------ c2' planner ---
 
 def test_eplb_plan_worked_example():
