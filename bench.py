@@ -49,6 +49,8 @@ def algorithmic(w):
         "dispatch_bytes": T * H * 2 + R * 4 + R * (H + 16) + 3 * R * 4 + w.D * w.S * 16,
         # read bf16 returns, row ids and weights, write the bf16 output
         "combine_bytes": R * H * 2 + R * 8 + T * H * 2,
+        # INT8 returns: read R rows of H codes + H/256 fp32 scales instead of bf16 rows
+        "combine_q8_bytes": R * (H + 4 * (H // 256)) + R * 8 + T * H * 2,
         # 2 ops per multiply-add: gate and up (2I outputs over K = H), down (H outputs over K = I)
         "gateup_ops": 2 * R * H * 2 * I,
         "down_ops": 2 * R * I * H,
@@ -93,13 +95,15 @@ def build_layer(w, log_every=64):
     return layer, x, lg
 
 
-def time_gpu(layer, x, lg, steps, warmup):
+def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
+    """Per-stage and per-step times of `steps` whole steps.  With int8_returns the
+    experts return INT8 rows (one scale per 256 columns) and the combine reads them."""
     import torch
     stages = [("route", lambda: layer.route(lg)),
               ("dispatch", lambda: layer.dispatch(x)),
               ("gateup", layer.experts_gateup),
-              ("down", layer.experts_down),
-              ("combine", lambda: layer.combine("bf16"))]
+              ("down", layer.experts_down_int8ret if int8_returns else layer.experts_down),
+              ("combine", lambda: layer.combine("q8blocks" if int8_returns else "bf16"))]
     for _ in range(warmup):
         for _, f in stages:
             f()
@@ -349,6 +353,20 @@ def main():
                      "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
     }
+    # the INT8 return path (XDS P089) timed the same way, reported beside the bf16 one
+    ms8, per8, dist8 = time_gpu(layer, x, lg, args.steps, args.warmup, int8_returns=True)
+    log(f"[bench] INT8 returns: {ms8:.3f} ms/step " +
+        " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per8.items()))
+    dc8_bytes = A["dispatch_bytes"] + A["combine_q8_bytes"]
+    dc8_ms = per8["dispatch"] + per8["combine"]
+    result["int8_returns"] = {
+        "tokens_per_s": round(w.T / (ms8 * 1e-3), 1), "ms_per_step": round(ms8, 4),
+        "stages_us": {k: round(v * 1e3, 2) for k, v in per8.items()},
+        "combine_GBps": round(A["combine_q8_bytes"] / (per8["combine"] * 1e-3) / 1e9, 1),
+        "dispatch_combine": {"GBps": round(dc8_bytes / (dc8_ms * 1e-3) / 1e9, 1),
+                             "bytes": dc8_bytes, "us": round(dc8_ms * 1e3, 2)},
+        "note": "expert returns quantized to INT8 in the down projection's epilogue (one "
+                "fp32 scale per 256 columns); not the headline configuration (bf16 returns)"}
     if not args.no_attainable:
         log("[bench] attainable rates: device copy, library INT8 GEMM")
         att = attainable(w)

@@ -27,11 +27,12 @@ MOE_DEVICE_OVER_CAPACITY = 4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATING_SOFTMAX, GATING_SIGMOID = 0, 1
-RET_Q8_FROM_DISPATCH, RET_BF16 = 0, 1
+RET_Q8_FROM_DISPATCH, RET_BF16, RET_Q8_BLOCKS = 0, 1, 2
+RET_Q8_BLOCK = 256  # columns per scale of the INT8 expert returns
 
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
-            "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8", "moe_relay_returns",
-            "moe_combine", "moe_status_string")
+            "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
+            "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -48,7 +49,8 @@ class Sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("msg_bytes", "cap_rows", "dispatch_bytes", "dispatch_bytes_per_partition",
                  "combine_bytes_per_partition", "relay_bytes", "return_bytes",
-                 "dispatch_scratch_bytes", "ffn_scratch_bytes")]
+                 "dispatch_scratch_bytes", "ffn_scratch_bytes", "ret_q8_row_bytes",
+                 "ret_q8_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -84,6 +86,7 @@ def lib():
                                            _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_down_q8.argtypes = [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(Geom), _P, _P, _P,
                                          ctypes.c_size_t, _P]
+        L.moe_expert_down_q8_int8ret.argtypes = L.moe_expert_down_q8.argtypes
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -201,6 +204,16 @@ def moe_expert_down_q8(slot_count, slot_offset, slot_logical, w_down, s_down, I:
                                     _ptr(acc_down_dbg), _ptr(scratch),
                                     scratch.numel() * scratch.element_size(), _stream(stream)),
            "moe_expert_down_q8")
+
+
+def moe_expert_down_q8_int8ret(slot_count, slot_offset, slot_logical, w_down, s_down, I: int,
+                               g: Geom, ret_q8, acc_down_dbg=None, scratch=None, stream=None):
+    _check(lib().moe_expert_down_q8_int8ret(_ptr(slot_count), _ptr(slot_offset),
+                                            _ptr(slot_logical), _ptr(w_down), _ptr(s_down), I,
+                                            ctypes.byref(g), _ptr(ret_q8), _ptr(acc_down_dbg),
+                                            _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                            _stream(stream)),
+           "moe_expert_down_q8_int8ret")
 
 
 def moe_relay_returns(ret, phys_ids, slot_partition, ret_row, g: Geom, comb_row, stream=None):

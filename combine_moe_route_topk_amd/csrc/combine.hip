@@ -17,7 +17,10 @@ namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <bool Q8, bool OUT_BF16, int KMAX>
+// Q8: INT8 value rows (codes at byte 0).  QB: their scales are per block of
+// MOE_RET_Q8_BLOCK columns from byte H (INT8 expert returns) instead of one
+// scale at byte H (dispatch messages).
+template <bool Q8, bool OUT_BF16, int KMAX, bool QB = false>
 __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict__ src,
                                                       const int32_t *__restrict__ row,
                                                       const float *__restrict__ topk_w, int T,
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
   if (lane < k) {
     my_row = row[t * k + lane];
     my_w = topk_w[t * k + lane];
-    if (Q8 && my_row >= 0) my_s = *(const float *)(src + my_row * row_bytes + H);
+    if (Q8 && !QB && my_row >= 0) my_s = *(const float *)(src + my_row * row_bytes + H);
   }
   const uint8_t *base[KMAX];
   float w[KMAX], sc[KMAX];
@@ -68,12 +71,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
       for (int j = 0; j < KMAX; ++j) {
         if (!base[j]) continue;
         const uint32_t *wd = (const uint32_t *)&v[u][j];
+        // a lane's 16 codes lie in one scale block (16 divides the block)
+        const float sj = QB ? *(const float *)(base[j] + H + 4 * (e0 / MOE_RET_Q8_BLOCK)) : sc[j];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           float x;
           if (Q8) {
             const int8_t q = (int8_t)((wd[e >> 2] >> (8 * (e & 3))) & 0xffu);
-            x = (float)q * sc[j];
+            x = (float)q * sj;
           } else {
             x = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
           }
@@ -101,16 +106,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
 }
 
 template <int KMAX>
-void launch_combine(bool q8, bool obf, dim3 grid, hipStream_t s, const uint8_t *src,
+void launch_combine(bool q8, bool qb, bool obf, dim3 grid, hipStream_t s, const uint8_t *src,
                     const int32_t *row, const float *w, const moe_geom_t &g, int64_t rb,
                     void *out) {
-#define MOE_COMBINE(Q, O)                                                                     \
-  hipLaunchKernelGGL((combine_kernel<Q, O, KMAX>), grid, dim3(256), 0, s, src, row, w, g.T, g.H, \
-                     g.k, rb, out)
-  if (q8 && obf) MOE_COMBINE(true, true);
-  else if (q8) MOE_COMBINE(true, false);
-  else if (obf) MOE_COMBINE(false, true);
-  else MOE_COMBINE(false, false);
+#define MOE_COMBINE(Q, O, B)                                                                     \
+  hipLaunchKernelGGL((combine_kernel<Q, O, KMAX, B>), grid, dim3(256), 0, s, src, row, w, g.T,    \
+                     g.H, g.k, rb, out)
+  if (qb && obf) MOE_COMBINE(true, true, true);
+  else if (qb) MOE_COMBINE(true, false, true);
+  else if (q8 && obf) MOE_COMBINE(true, true, false);
+  else if (q8) MOE_COMBINE(true, false, false);
+  else if (obf) MOE_COMBINE(false, true, false);
+  else MOE_COMBINE(false, false, false);
 #undef MOE_COMBINE
 }
 
@@ -125,24 +132,26 @@ extern "C" int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *
   int st = validate_geom(g);
   if (st != MOE_OK) return st;
   if (g->T > 0 && (!src || !row || !topk_w || !out)) return MOE_ERR_INVALID_ARG;
-  if (mode != MOE_RET_Q8_FROM_DISPATCH && mode != MOE_RET_BF16) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_RET_Q8_FROM_DISPATCH && mode != MOE_RET_BF16 && mode != MOE_RET_Q8_BLOCKS)
+    return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if (g->T == 0) return MOE_OK;
-  const bool q8 = mode == MOE_RET_Q8_FROM_DISPATCH;
-  const int64_t rb = q8 ? msg_bytes_of(*g) : (int64_t)g->H * 2;
+  const bool qb = mode == MOE_RET_Q8_BLOCKS;
+  const bool q8 = mode == MOE_RET_Q8_FROM_DISPATCH || qb;
+  const int64_t rb = qb ? ret_q8_row_bytes_of(*g) : q8 ? msg_bytes_of(*g) : (int64_t)g->H * 2;
   const dim3 grid((unsigned)((g->T + 3) / 4));
   hipStream_t s = (hipStream_t)stream;
   const bool obf = out_dtype == MOE_DTYPE_BF16;
   const uint8_t *sp = (const uint8_t *)src;
   if (g->k <= 2)
-    launch_combine<2>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+    launch_combine<2>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
   else if (g->k <= 4)
-    launch_combine<4>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+    launch_combine<4>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
   else if (g->k <= 8)
-    launch_combine<8>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+    launch_combine<8>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
   else
-    launch_combine<16>(q8, obf, grid, s, sp, row, topk_w, *g, rb, out);
+    launch_combine<16>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
   return launch_status();
 }
 

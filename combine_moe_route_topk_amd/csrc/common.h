@@ -14,6 +14,11 @@ inline int64_t msg_bytes_of(const moe_geom_t &g) {
   return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 127) / 128) * 128;
 }
 inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
+// INT8 return row: H codes, then one fp32 scale per MOE_RET_Q8_BLOCK columns, 16-byte rows
+inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
+  const int64_t nblk = ((int64_t)g.H + MOE_RET_Q8_BLOCK - 1) / MOE_RET_Q8_BLOCK;
+  return ((int64_t)g.H + 4 * nblk + 15) / 16 * 16;
+}
 
 // Routes per dispatch chunk: chunks never straddle a source partition.
 constexpr int kChunkRoutes = 256;

@@ -127,7 +127,9 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 // 32-wide K sub-step per wave.  The DMA of step kt + 2 is in flight while
 // step kt feeds the MFMAs from LDS; one barrier per K step; two blocks per CU
 // overlap each other's waits.
-template <int MODE, bool DBG>
+// Q8OUT (DOWN only): the return rows are INT8 with one fp32 scale per 256
+// columns (the n-tile) instead of bf16 -- see the epilogue.
+template <int MODE, bool DBG, bool Q8OUT = false>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_count,
     const int32_t *__restrict__ slot_offset, const int32_t *__restrict__ slot_logical,
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const int8_t *__restrict__ hq, const float *__restrict__ hs, const int8_t *__restrict__ w,
     const float *__restrict__ wscale, int P, int E, int H, int I, int64_t nrows,
     float *__restrict__ h_out, float *__restrict__ pmax, uint16_t *__restrict__ ret,
-    int32_t *__restrict__ acc_dbg) {
+    int64_t ret_row_bytes, int32_t *__restrict__ acc_dbg) {
   constexpr int MB = BM / 32, NB = 2;       // MFMA blocks per wave
   // one LDS arena: the K-step ring (A stages, then B stages) during the main
   // loop, then the output staging of the epilogue
@@ -362,6 +364,55 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       }
     }
     __syncthreads();
+    if constexpr (Q8OUT) {
+      // INT8 returns [XDS DeepSeek INT8 量化, P089: expert outputs quantized
+      // before they travel back]: the staged bf16 tile is what the bf16 path
+      // returns; each row's 256 columns (one block) get the token rule --
+      // amax over the block, s = amax / 127, q = clamp(rne(y / s), +-127).
+      // Columns past H staged 0, so they do not move the amax.  Row layout:
+      // H codes, then ceil(H / 256) fp32 block scales.
+      __shared__ float qscale[BM];
+      uint8_t *retq = (uint8_t *)ret;
+      if (tid < BM) {
+        const uint4 *rowp = (const uint4 *)((const uint8_t *)stb + tid * kStageStrideB);
+        float m = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < BN / 8; ++c) {
+          const uint4 v = rowp[c];
+          const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wd[q] & 0xffffu)), fabsf(bf16_bits_to_f32(wd[q] >> 16))));
+        }
+        const float sq = m / 127.0f;
+        qscale[tid] = sq;
+        const int64_t rr = row0 + tid;
+        if (tid < rows_here && rr < nrows) *(float *)(retq + rr * ret_row_bytes + H + 4 * tl.n) = sq;
+      }
+      __syncthreads();
+      // 128 rows x 256 columns = 2048 chunks of 16 codes -> one 16-byte store each
+#pragma unroll 2
+      for (int q = tid; q < BM * (BN / 16); q += 256) {
+        const int lr = q >> 4, c16 = (q & 15) * 16;
+        const int64_t rr = row0 + lr;
+        if (lr < rows_here && rr < nrows && n0 + c16 < H) {
+          const float sq = qscale[lr];
+          const uint4 *src = (const uint4 *)((const uint8_t *)stb + lr * kStageStrideB + c16 * 2);
+          const uint4 a = src[0], b = src[1];
+          const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float y = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            int code = 0;
+            if (sq != 0.0f) code = (int)fminf(fmaxf(rintf(y / sq), -127.0f), 127.0f);
+            pk[e >> 2] |= ((uint32_t)code & 0xffu) << (8 * (e & 3));
+          }
+          *(uint4 *)(retq + rr * ret_row_bytes + n0 + c16) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      }
+      return;
+    }
     // 128 rows x 256 columns = 4096 chunks of 8 bf16 -> one 16-byte store each
 #pragma unroll 4
     for (int q = tid; q < BM * (BN / 8); q += 256) {
@@ -497,7 +548,8 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP, DBG>), grid, dim3(256), 0, s, a->tiles, slot_count, \
                      slot_offset, slot_logical, slot_rows, (const uint8_t *)disp_buf, a->msg,      \
                      (const int8_t *)nullptr, (const float *)nullptr, w_gateup, s_gateup, g->P,    \
-                     g->E, g->H, I, a->nrows, a->h, a->pmax, (uint16_t *)nullptr, acc_gateup_dbg)
+                     g->E, g->H, I, a->nrows, a->h, a->pmax, (uint16_t *)nullptr, (int64_t)0,      \
+                     acc_gateup_dbg)
   if (acc_gateup_dbg)
     MOE_GATEUP(true);
   else
@@ -506,15 +558,19 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   return launch_status();
 }
 
-extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
-                                  const int32_t *slot_logical, const int8_t *w_down,
-                                  const float *s_down, int32_t I, const moe_geom_t *g,
-                                  uint16_t *ret, int32_t *acc_down_dbg, void *scratch,
-                                  size_t scratch_bytes, void *stream) {
+namespace moe {
+namespace {
+
+// requant + down GEMM; ret is bf16 [T*k][H], or with q8out the INT8 return rows
+int expert_down(const int32_t *slot_count, const int32_t *slot_offset,
+                const int32_t *slot_logical, const int8_t *w_down, const float *s_down, int32_t I,
+                const moe_geom_t *g, void *ret, bool q8out, int32_t *acc_down_dbg, void *scratch,
+                size_t scratch_bytes, void *stream) {
   FfnArgs args{};
   FfnArgs *a = &args;
   int st = ffn_common(g, I, scratch, scratch_bytes, a);
   if (st != MOE_OK) return st;
+  if (q8out && g->relays > 0) return MOE_ERR_UNSUPPORTED;  // the E2A hop moves bf16 rows
   if (a->nrows == 0) return MOE_OK;
   if (!slot_count || !slot_offset || !slot_logical || !w_down || !s_down || !ret)
     return MOE_ERR_INVALID_ARG;
@@ -524,17 +580,42 @@ extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot
                      a->h, a->pmax, slot_offset, g->P, I, a->nrows, a->hq, a->hs);
   if ((st = launch_status()) != MOE_OK) return st;
   const dim3 grid = gemm_grid(a->mt_bound, (g->H + BN - 1) / BN);
-#define MOE_DOWN(DBG)                                                                           \
-  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN, DBG>), grid, dim3(256), 0, s, a->tiles, slot_count,   \
+  const int64_t rb = q8out ? ret_q8_row_bytes_of(*g) : (int64_t)g->H * 2;
+#define MOE_DOWN(DBG, Q)                                                                        \
+  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN, DBG, Q>), grid, dim3(256), 0, s, a->tiles, slot_count, \
                      slot_offset, slot_logical, (const int32_t *)nullptr, (const uint8_t *)nullptr, \
                      a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E, g->H, I, a->nrows,          \
-                     (float *)nullptr, (float *)nullptr, ret, acc_down_dbg)
-  if (acc_down_dbg)
-    MOE_DOWN(true);
-  else
-    MOE_DOWN(false);
+                     (float *)nullptr, (float *)nullptr, (uint16_t *)ret, rb, acc_down_dbg)
+  if (q8out) {
+    if (acc_down_dbg) MOE_DOWN(true, true);
+    else MOE_DOWN(false, true);
+  } else {
+    if (acc_down_dbg) MOE_DOWN(true, false);
+    else MOE_DOWN(false, false);
+  }
 #undef MOE_DOWN
   return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
+                                  const int32_t *slot_logical, const int8_t *w_down,
+                                  const float *s_down, int32_t I, const moe_geom_t *g,
+                                  uint16_t *ret, int32_t *acc_down_dbg, void *scratch,
+                                  size_t scratch_bytes, void *stream) {
+  return expert_down(slot_count, slot_offset, slot_logical, w_down, s_down, I, g, ret, false,
+                     acc_down_dbg, scratch, scratch_bytes, stream);
+}
+
+extern "C" int moe_expert_down_q8_int8ret(const int32_t *slot_count, const int32_t *slot_offset,
+                                          const int32_t *slot_logical, const int8_t *w_down,
+                                          const float *s_down, int32_t I, const moe_geom_t *g,
+                                          void *ret_q8, int32_t *acc_down_dbg, void *scratch,
+                                          size_t scratch_bytes, void *stream) {
+  return expert_down(slot_count, slot_offset, slot_logical, w_down, s_down, I, g, ret_q8, true,
+                     acc_down_dbg, scratch, scratch_bytes, stream);
 }
 
 extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count,

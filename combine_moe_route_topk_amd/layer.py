@@ -13,10 +13,10 @@ from typing import Optional
 
 import torch
 
-from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16,
+from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16, RET_Q8_BLOCKS,
                RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_down_q8,
-               moe_expert_ffn_q8, moe_expert_gateup_q8, moe_plan_sizes, moe_relay_returns,
-               moe_route_topk)
+               moe_expert_down_q8_int8ret, moe_expert_ffn_q8, moe_expert_gateup_q8,
+               moe_plan_sizes, moe_relay_returns, moe_route_topk)
 
 
 class MoeBuffers:
@@ -47,6 +47,13 @@ class MoeBuffers:
         self.ret = torch.empty((nret, H), dtype=torch.int16, device=device)
         self.comb_row = torch.empty((T, k), **i32) if g.relays else None
         self.out = torch.empty((T, H), dtype=out_dtype, device=device)
+
+    def ret_q8_rows(self):
+        """INT8 expert return rows [T*k][ret_q8_row_bytes] bytes (allocated on first use)."""
+        if getattr(self, "_ret_q8", None) is None:
+            self._ret_q8 = torch.empty((self.g.T * self.g.k, self.sizes.ret_q8_row_bytes),
+                                       dtype=torch.uint8, device=self.out.device)
+        return self._ret_q8
 
     def disp_rows_view(self):
         """The dispatch buffer as [D*S*cap][msg] bytes."""
@@ -111,11 +118,22 @@ class MoeLayer:
         moe_expert_down_q8(b.slot_count, b.slot_offset, self.slot_logical, wd, sd, self.I, self.g,
                            b.ret, None, b.fscratch)
 
+    def experts_down_int8ret(self, acc_down_dbg=None):
+        """Down projection with INT8 return rows (one scale per 256 columns)."""
+        b = self.buf
+        _, _, wd, sd = self.weights
+        moe_expert_down_q8_int8ret(b.slot_count, b.slot_offset, self.slot_logical, wd, sd, self.I,
+                                   self.g, b.ret_q8_rows(), acc_down_dbg, b.fscratch)
+
     def combine(self, mode: str):
+        """mode 'q8' (identity experts: dispatched messages), 'bf16' (bf16 returns) or
+        'q8blocks' (INT8 returns of experts_down_int8ret)."""
         b = self.buf
         odt = DTYPE_BF16 if self.out_dtype == torch.bfloat16 else DTYPE_F32
         if mode == "q8":
             moe_combine(RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, b.topk_w, self.g, odt, b.out)
+        elif mode == "q8blocks":
+            moe_combine(RET_Q8_BLOCKS, b.ret_q8_rows(), b.ret_row, b.topk_w, self.g, odt, b.out)
         else:
             row = b.ret_row
             if self.g.relays:
@@ -124,9 +142,15 @@ class MoeLayer:
             moe_combine(RET_BF16, b.ret, row, b.topk_w, self.g, odt, b.out)
 
     def forward(self, x, logits, combine: str = "bf16"):
+        """route -> dispatch -> experts -> combine; combine 'q8blocks' runs the experts
+        with INT8 return rows."""
         self.route(logits)
         self.dispatch(x)
         if self.weights is not None:
-            self.experts()
+            if combine == "q8blocks":
+                self.experts_gateup()
+                self.experts_down_int8ret()
+            else:
+                self.experts()
         self.combine(combine)
         return self.buf.out

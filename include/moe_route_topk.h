@@ -78,8 +78,13 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_GATING_SOFTMAX = 0, MOE_GATING_SIGMOID = 1 } moe_gating_t;
 typedef enum {
   MOE_RET_Q8_FROM_DISPATCH = 0, /* value rows are dispatch messages (int8 + scale) */
-  MOE_RET_BF16 = 1              /* value rows are bf16 expert returns              */
+  MOE_RET_BF16 = 1,             /* value rows are bf16 expert returns              */
+  MOE_RET_Q8_BLOCKS = 2         /* value rows are INT8 expert returns: H codes and */
+                                /* one fp32 scale per MOE_RET_Q8_BLOCK columns     */
 } moe_ret_mode_t;
+
+/* Columns per scale of the INT8 expert returns (the down projection's n-tile). */
+#define MOE_RET_Q8_BLOCK 256
 
 /* Geometry of one MoE layer call. */
 typedef struct moe_geom {
@@ -118,6 +123,8 @@ typedef struct moe_sizes {
                                        /* when relays > 0 (E2A staging follows the rows)  */
   int64_t dispatch_scratch_bytes;      /* scratch of moe_dispatch_q8                      */
   int64_t ffn_scratch_bytes;           /* scratch of moe_expert_ffn_q8 (I > 0)            */
+  int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256), 16B   */
+  int64_t ret_q8_bytes;                /* T * k INT8 return rows                          */
 } moe_sizes_t;
 
 /*
@@ -262,6 +269,27 @@ int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
                        void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * moe_expert_down_q8_int8ret -- moe_expert_down_q8 with INT8 return rows
+ * [XDS DeepSeek INT8 量化, P089: expert outputs are quantized to INT8 before
+ * they travel back, the quantization fused into the transfer].  The bf16 value
+ * y that moe_expert_down_q8 would return is quantized in the projection's
+ * epilogue, one scale per MOE_RET_Q8_BLOCK columns of each row (the pages do
+ * not fix the granularity; 256 columns is the projection's output tile):
+ *   s = max |y| over the block / 127,  q = clamp(round_half_even(y / s), +-127)
+ *   (fp32 divisions; an all-zero block gives s = 0, q = 0).
+ *   ret_q8  [T*k][ret_q8_row_bytes] (moe_plan_sizes): row slot_offset[p] + i
+ *           holds H int8 codes, then ceil(H / 256) fp32 scales; 16B.
+ * Combine these rows with mode MOE_RET_Q8_BLOCKS.  Geometries with relays are
+ * not supported (MOE_ERR_UNSUPPORTED): the E2A hop moves bf16 rows.
+ * Other arguments, preconditions and errors as moe_expert_down_q8.
+ */
+int moe_expert_down_q8_int8ret(const int32_t *slot_count, const int32_t *slot_offset,
+                               const int32_t *slot_logical, const int8_t *w_down,
+                               const float *s_down, int32_t I, const moe_geom_t *g, void *ret_q8,
+                               int32_t *acc_down_dbg, void *scratch, size_t scratch_bytes,
+                               void *stream);
+
+/*
  * moe_relay_returns -- E2A second hop of the two-hop trampoline [XDS 解耦 A2A,
  * P045, Fig. 8: E2A runs the A2E path in reverse].  With g->relays = R > 0, the
  * return row of every route whose slot lives on a partition d >= R is copied
@@ -282,6 +310,8 @@ int moe_relay_returns(uint16_t *ret, const int32_t *phys_ids, const int32_t *slo
  *   mode Q8_FROM_DISPATCH: src = disp_buf, row = disp_row; v = f32(q) * scale
  *                          (identity experts: the dispatched message is the value)
  *   mode BF16:             src = ret [rows][H] bf16, row = ret_row (or comb_row)
+ *   mode Q8_BLOCKS:        src = ret_q8 (moe_expert_down_q8_int8ret), row = ret_row;
+ *                          v = f32(q[c]) * scale[c / 256] [XDS DeepSeek INT8 量化, P089]
  *   topk_w  [T][k] fp32;  out [T][H] fp32 or bf16 (out_dtype, RNE), 16B.
  *   Routes with row < 0 contribute nothing.
  */

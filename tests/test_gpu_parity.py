@@ -324,6 +324,68 @@ def test_layer_ffn_small_end_to_end():
     assert_close(bf16_to_f32(out), bf16_to_f32(r["out"]), BF16_RTOL, BF16_ATOL, "layer output")
 
 
+def _int8_return_rows_oracle(w, y_rows, rb):
+    q, sblk = oracle.quant_blocks(y_rows, moe.RET_Q8_BLOCK)
+    return oracle.int8_return_rows(q, sblk, rb)
+
+
+def test_expert_int8_returns_and_combine_small():
+    """INT8 expert returns (XDS P089): the down projection's INT8 rows (codes and
+    one scale per 256 columns, the last block half full at H = 384) are bit-exact
+    against the oracle's block quantization of its bf16 returns, the down
+    accumulators are unchanged, and the combine of those rows matches the
+    oracle's combine of the same rows bit for bit (fp32 and bf16 outputs)."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
+    n = w.T * w.k
+    b = c.layer.buf
+    rb = b.sizes.ret_q8_row_bytes
+    assert rb == ((w.H + 4 * 2 + 15) // 16) * 16
+    acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
+    c.layer.experts_gateup()
+    c.layer.experts_down_int8ret(acc_d)
+    torch.cuda.synchronize()
+    got = host(b.ret_q8_rows())
+    ad = host(acc_d)
+    logical = c.sl[phys.ravel()]
+    rr = lay["ret_row"].ravel()
+    nb = w.H + 4 * 2
+    for e in np.unique(logical):
+        sel = np.nonzero(logical == e)[0]
+        toks = sel // w.k
+        y, _, _, _, o_d = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e],
+                                            want_acc=True)
+        assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
+        exp = _int8_return_rows_oracle(w, y, rb)
+        assert np.array_equal(got[rr[sel], :nb], exp[:, :nb]), f"INT8 return rows, expert {e}"
+    w32 = host(b.topk_w)
+    for odt, obf in ((torch.float32, False), (torch.bfloat16, True)):
+        c.layer.out_dtype = odt
+        b.out = torch.empty((w.T, w.H), dtype=odt, device="cuda")
+        c.layer.combine("q8blocks")
+        torch.cuda.synchronize()
+        ref = oracle.combine(got, lay["ret_row"], w32, w.k, w.H, "q8blocks", obf,
+                             scale_offset=w.H, scale_block=moe.RET_Q8_BLOCK)
+        out = host(b.out.view(torch.int16)).view(np.uint16) if obf else host(b.out)
+        assert np.array_equal(out, ref), f"combine of INT8 returns ({odt})"
+
+
+def test_layer_int8_returns_small_end_to_end():
+    """route -> dispatch -> experts with INT8 returns -> combine, against the
+    oracle's whole path (its bf16 returns quantized per 256-column block and
+    combined in the same mode)."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), weights = _ffn_case(w)
+    out = host(c.layer.forward(c.x_d, c.lg_d, combine="q8blocks").view(torch.int16)).view(np.uint16)
+    r = oracle.moe_layer(w, c.x, c.lg, c.bias, None, None, c.sp, c.sl, event_id=1, weights=weights)
+    rb = c.layer.buf.sizes.ret_q8_row_bytes
+    rows = _int8_return_rows_oracle(w, r["route_returns"], rb)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    ref = oracle.combine(rows, ident, r["topk_w32"], w.k, w.H, "q8blocks", True,
+                         scale_offset=w.H, scale_block=moe.RET_Q8_BLOCK)
+    assert_close(bf16_to_f32(out), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL, "layer output")
+
+
 def test_expert_ffn_layer12288_sampled_rows():
     """The headline layer (T=12288, 256 experts, I=2048, Zipf routing), launched as
     the bench launches it; the oracle recomputes 32 rows of each of four slots
@@ -347,6 +409,11 @@ def test_expert_ffn_layer12288_sampled_rows():
     rng = np.random.default_rng(0)
     slots = {int(np.argmax(sc)), int(nz[np.argmin(sc[nz])])} | set(rng.choice(nz, 2).tolist())
     inv = np.argsort(lay["ret_row"].ravel())  # ret row -> route index
+    c.layer.experts_down_int8ret()  # INT8 returns from the same h (scratch still holds it)
+    torch.cuda.synchronize()
+    q8 = host(b.ret_q8_rows())
+    rb = b.sizes.ret_q8_row_bytes
+    nb = w.H + 4 * (w.H // moe.RET_Q8_BLOCK)
     for p in sorted(slots):
         o = lay["slot_offset"][p]
         rows = np.arange(o, o + sc[p])
@@ -357,6 +424,8 @@ def test_expert_ffn_layer12288_sampled_rows():
         e = c.sl[p]
         y, *_ = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e])
         assert np.array_equal(ret[rows], y), f"slot {p} (expert {e}, {sc[p]} rows)"
+        exp = _int8_return_rows_oracle(w, y, rb)
+        assert np.array_equal(q8[rows, :nb], exp[:, :nb]), f"INT8 returns, slot {p}"
 
 
 # ------------------------------------------------------------ edge cases ---
