@@ -130,11 +130,11 @@ __device__ __forceinline__ int block_incl_scan_256(int v, int *sh) {
 
 // Block b < D scans hist_d row b and writes meta[b][s] = {event, prefix at
 // s's first chunk, count} for every source s; block D + p scans hist_p row p
-// and writes slot_count[p].  Scans are exclusive over the nc chunks, the total
-// goes to column nc.  The last slot block to finish (an agent-scope
-// acquire-release counter, zeroed by the count kernel) prefixes the slot
-// totals into slot_offset and writes slot_local; block 0 clears the status
-// word, so no separate finalize launch is needed.
+// and writes slot_count[p] and slot_local[p].  Scans are exclusive over the nc
+// chunks, the total goes to column nc.  The last slot block to finish (an
+// agent-scope acquire-release counter, zeroed by the count kernel) prefixes
+// the slot totals into slot_offset; block 0 clears the status word, so no
+// separate finalize launch is needed.
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     int32_t *__restrict__ hist_d, int32_t *__restrict__ hist_p,
     const int32_t *__restrict__ slot_partition, int D, int P, int S, int cps, int nc,
@@ -144,7 +144,6 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
   __shared__ int sh[4];
   __shared__ int carry_sh;
   __shared__ int last;
-  __shared__ int part[MOE_MAX_P];
   const bool is_d = blockIdx.x < (unsigned)D;
   const int row = is_d ? blockIdx.x : blockIdx.x - D;
   int32_t *h = (is_d ? hist_d : hist_p) + (int64_t)row * (nc + 1);
@@ -174,6 +173,16 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
     return;
   }
+  // slot_local[row]: index of the slot among the slots of its partition
+  {
+    const int d = slot_partition[row];
+    int nloc = 0;
+    for (int q = threadIdx.x; q < row; q += 256) nloc += slot_partition[q] == d;
+    for (int o = 32; o > 0; o >>= 1) nloc += __shfl_xor(nloc, o, 64);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = nloc;
+    __syncthreads();
+    if (threadIdx.x == 0) slot_local[row] = sh[0] + sh[1] + sh[2] + sh[3];
+  }
   if (threadIdx.x == 0) {
     slot_count[row] = carry;
     // release: this block's total is visible before the count goes up
@@ -194,14 +203,6 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) slot_offset[P] = off;
-  for (int q = threadIdx.x; q < P; q += 256) part[q] = slot_partition[q];
-  __syncthreads();
-  for (int q = threadIdx.x; q < P; q += 256) {
-    const int d = part[q];
-    int nloc = 0;
-    for (int r = 0; r < q; ++r) nloc += part[r] == d;
-    slot_local[q] = nloc;
-  }
 }
 
 // -------------------------------------------------------------- scatter ---
