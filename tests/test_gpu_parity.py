@@ -158,6 +158,75 @@ def test_dispatch_parity_eplb4096_full():
     _check_dispatch(c, phys)
 
 
+def test_expert_ffn_eplb4096_replicas_sampled_rows():
+    """The EPLB layer at full size (T = 4096, 288 physical slots: 256 primaries and
+    32 replicas from the planner, INT8 SwiGLU experts, I = 2048), launched as a
+    caller would: the bf16 return rows of sampled rows are bit-exact against the
+    oracle -- for the hottest primary, its replicas (which share the logical
+    expert's weights) and two random slots -- and the layer output is within
+    bf16 tolerance of the oracle's on sampled tokens."""
+    w = mw.WORKLOADS["eplb4096"]
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    c.layer.dispatch(c.x_d)
+    q, s = oracle.quant_tokens(c.x, True)
+    lay = oracle.dispatch_layout(w, phys, c.sp, 1)
+    _log("[eplb4096] generating weights of the routed experts")
+    routed = np.unique(c.sl[phys.ravel()])
+    dev = dict(device="cuda")
+    wgu_d = torch.zeros((w.E, 2 * w.I, w.H), dtype=torch.int8, **dev)
+    sgu_d = torch.zeros((w.E, 2 * w.I), dtype=torch.float32, **dev)
+    wd_d = torch.zeros((w.E, w.H, w.I), dtype=torch.int8, **dev)
+    sd_d = torch.zeros((w.E, w.H), dtype=torch.float32, **dev)
+    host_w = {}
+    for e in routed:
+        a, b, c2, d = mw.expert_weights(w, int(e))
+        host_w[int(e)] = (a, b, c2, d)
+        wgu_d[e].copy_(torch.from_numpy(a))
+        sgu_d[e].copy_(torch.from_numpy(b))
+        wd_d[e].copy_(torch.from_numpy(c2))
+        sd_d[e].copy_(torch.from_numpy(d))
+    c.layer.weights = (wgu_d, sgu_d, wd_d, sd_d)
+    c.layer.I = w.I
+    c.layer.experts()
+    c.layer.combine("bf16")
+    torch.cuda.synchronize()
+    b = c.layer.buf
+    assert np.array_equal(host(b.ret_row), lay["ret_row"])
+    ret = host(b.ret.view(torch.int16)).view(np.uint16)
+    sc = lay["slot_count"]
+    hot = int(np.argmax(sc[:w.E]))
+    reps = [int(p) for p in range(w.E, w.P) if c.sl[p] == c.sl[hot] and sc[p] > 0]
+    assert reps, "the hottest expert has a replica under the planner"
+    rng = np.random.default_rng(1)
+    nz = np.nonzero(sc)[0]
+    slots = sorted({hot, *reps, *rng.choice(nz, 2).tolist()})
+    inv = np.argsort(lay["ret_row"].ravel())
+    for p in slots:
+        o = lay["slot_offset"][p]
+        rows = np.arange(o, o + sc[p])
+        if len(rows) > 24:
+            rows = np.sort(rng.choice(rows, 24, replace=False))
+        toks = inv[rows] // w.k
+        e = int(c.sl[p])
+        y, *_ = oracle.expert_ffn(q[toks], s[toks], *host_w[e])
+        assert np.array_equal(ret[rows], y), f"slot {p} (expert {e}, {sc[p]} rows)"
+    # layer output of sampled tokens: oracle combine of the oracle's returns
+    tsel = np.sort(rng.choice(w.T, 16, replace=False))
+    out = host(b.out.view(torch.int16)).view(np.uint16)
+    rr = lay["ret_row"]
+    logical = c.sl[phys]
+    vals = np.empty((len(tsel) * w.k, w.H), np.uint16)
+    for i, t in enumerate(tsel):
+        for j in range(w.k):
+            e = int(logical[t, j])
+            y, *_ = oracle.expert_ffn(q[t:t + 1], s[t:t + 1], *host_w[e])
+            vals[i * w.k + j] = y[0]
+    ident = np.arange(len(tsel) * w.k, dtype=np.int32).reshape(len(tsel), w.k)
+    ref = oracle.combine(vals, ident, tw[tsel].astype(np.float32), w.k, w.H, "bf16", True)
+    assert_close(bf16_to_f32(out[tsel]), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL, "layer output")
+
+
 def test_dispatch_twohop_small_equals_direct():
     """Two-hop (relays = 4): layout and rows equal the oracle's one-hop layout,
     and a direct run (relays = 0) writes the same bytes."""
