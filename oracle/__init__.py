@@ -37,9 +37,11 @@ def lib():
         L.orc_expert_ffn.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.orc_combine.argtypes = [_I32, _I32, _I32, _I32, _P, _I64, _I64, _I32, _P, _P, _I32, _P]
         L.orc_quant_blocks.argtypes = [_I32, _I32, _I32, _P, _P, _P]
+        L.orc_router_logits.argtypes = [_I32, _I32, _I32, _P, _P, _P]
         L.orc_eplb_plan.argtypes = [_I32, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]
         L.orc_static_buffer.argtypes = [_I64, _I64, _I64, _I64, _I64, _P]
         for f in ("orc_route_topk", "orc_eplb_phys", "orc_quant_tokens", "orc_quant_blocks",
+                  "orc_router_logits",
                   "orc_dispatch_layout",
                   "orc_dispatch_rows", "orc_expert_ffn", "orc_combine", "orc_eplb_plan",
                   "orc_static_buffer"):
@@ -78,6 +80,18 @@ def set_threads(n: int):
 
 
 # ------------------------------------------------------------------ steps ---
+
+def router_logits(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Exact gate logits of bf16 hidden states x [T][H] and gate weights w [E][H]
+    (bit patterns): float64 [T][E]."""
+    x = np.ascontiguousarray(x, np.uint16)
+    w = np.ascontiguousarray(w, np.uint16)
+    T, H = x.shape
+    E = w.shape[0]
+    out = np.empty((T, E), np.float64)
+    _check(lib().orc_router_logits(T, E, H, _p(x), _p(w), _p(out)), "router_logits")
+    return out
+
 
 def route_topk(logits: np.ndarray, k: int, gating: str, bias: Optional[np.ndarray] = None,
                logits_bf16: bool = False):

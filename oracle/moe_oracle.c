@@ -60,6 +60,31 @@ static float orc_load(const void *base, int64_t idx, int is_bf16) {
   return ((const float *)base)[idx];
 }
 
+/* ------------------------------------------------------ c0': gate logits -- */
+/*
+ * The gate's logits from the hidden states [CMI EP320 fused_moe listing:
+ * gate.topk(hidden, k = 8); CMI "INT8：少搬一些": gating stays in BF16/FP32]:
+ *   logits[t][e] = sum_h x[t][h] * w[e][h]
+ * with x, w bf16.  Each product of two bf16 values is exact in double and the
+ * double sum of H <= 16384 such products carries a relative error below
+ * H * 2^-53, far below any fp32 result's rounding: this is the exact value to
+ * compare an fp32 computation against.
+ */
+int orc_router_logits(int32_t T, int32_t E, int32_t H, const uint16_t *x, const uint16_t *w,
+                      double *logits) {
+  if (T < 0 || E <= 0 || H <= 0 || !x || !w || !logits) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h)
+        acc += (double)orc_bf16_to_f32(x[t * H + h]) * (double)orc_bf16_to_f32(w[e * H + h]);
+      logits[t * E + e] = acc;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---------------------------------------------------------- c1: top-k -- */
 /*
  * Gate top-k [XDS 合设 A2A, P038: routing indices and weights I, W in R^{B x k};

@@ -28,6 +28,28 @@ def _bf16_to_f32(b):
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# ------------------------------------------------------- c0' gate logits ---
+
+def test_router_logits_exact_on_integers_and_library_on_floats():
+    """Gate logits: with small-integer bf16 inputs every dot product is an exact
+    integer (int64 matmul); with N(0,1) inputs they equal a float64 library
+    matmul of the decoded values to double rounding."""
+    rng = np.random.default_rng(31)
+    T, E, H = 24, 12, 352
+    xi = rng.integers(-8, 9, (T, H))
+    wi = rng.integers(-8, 9, (E, H))
+    xb = mw.to_bf16_bits(xi.astype(np.float32))
+    wb = mw.to_bf16_bits(wi.astype(np.float32))
+    got = oracle.router_logits(xb, wb)
+    assert np.array_equal(got, (xi @ wi.T).astype(np.float64))
+    xb = mw.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = mw.to_bf16_bits((rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+    got = oracle.router_logits(xb, wb)
+    ref = _bf16_to_f32(xb).astype(np.float64) @ _bf16_to_f32(wb).astype(np.float64).T
+    mag = np.abs(_bf16_to_f32(xb)).astype(np.float64) @ np.abs(_bf16_to_f32(wb)).astype(np.float64).T
+    assert np.all(np.abs(got - ref) <= 1e-13 * mag)
+
+
 # ------------------------------------------------------------- c1 top-k ---
 
 @pytest.mark.parametrize("E,k,gating,bf16", [(8, 2, "softmax", False), (16, 5, "sigmoid", True),
