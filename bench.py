@@ -130,6 +130,31 @@ def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
     return total_ms / steps, per, dist
 
 
+def time_router(layer, x, w, steps, warmup):
+    """moe_router_logits on the layer's hidden states: x [T][H] . W_router^T -> fp32 [T][E]."""
+    import numpy as np
+    import torch
+    import moe_workloads as mw
+    wr = torch.from_numpy(mw.router_weights(w).view(np.int16)).view(torch.bfloat16).cuda()
+    for _ in range(warmup):
+        layer.router(x, wr)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        layer.router(x, wr)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    flops = 2.0 * w.T * w.E * w.H
+    nbytes = w.T * w.H * 2 + w.E * w.H * 2 + w.T * w.E * 4
+    return {"us": round(us, 2), "TFLOPS": round(flops / (us * 1e-6) / 1e12, 1),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "splits": int(layer.buf.sizes.router_scratch_bytes // (w.T * w.E * 4)),
+            "note": "bf16 MFMA, fp32 accumulation; timed alone (the workload's step starts "
+                    "from the logits)"}
+
+
 def attainable(w, reps=5):
     """Attainable rates on this GPU, for context next to the published peaks: a
     plain 1 GiB device copy (HBM) and the vendor library's dense INT8 GEMM
@@ -367,6 +392,10 @@ def main():
                              "bytes": dc8_bytes, "us": round(dc8_ms * 1e3, 2)},
         "note": "expert returns quantized to INT8 in the down projection's epilogue (one "
                 "fp32 scale per 256 columns); not the headline configuration (bf16 returns)"}
+    # the gate's logits from the hidden states (bf16 MFMA, split-K), timed alone:
+    # the headline step starts from the logits, as the workload defines
+    result["router"] = time_router(layer, x, w, args.steps, args.warmup)
+    log(f"[bench] router logits: {result['router']['us']:.1f} us")
     if not args.no_attainable:
         log("[bench] attainable rates: device copy, library INT8 GEMM")
         att = attainable(w)

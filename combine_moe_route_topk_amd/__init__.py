@@ -32,7 +32,8 @@ RET_Q8_BLOCK = 256  # columns per scale of the INT8 expert returns
 
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
-            "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_status_string")
+            "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
+            "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -50,7 +51,7 @@ class Sizes(ctypes.Structure):
                 ("msg_bytes", "cap_rows", "dispatch_bytes", "dispatch_bytes_per_partition",
                  "combine_bytes_per_partition", "relay_bytes", "return_bytes",
                  "dispatch_scratch_bytes", "ffn_scratch_bytes", "ret_q8_row_bytes",
-                 "ret_q8_bytes")]
+                 "ret_q8_bytes", "router_scratch_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -87,6 +88,7 @@ def lib():
         L.moe_expert_down_q8.argtypes = [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(Geom), _P, _P, _P,
                                          ctypes.c_size_t, _P]
         L.moe_expert_down_q8_int8ret.argtypes = L.moe_expert_down_q8.argtypes
+        L.moe_router_logits.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P, ctypes.c_size_t, _P]
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +216,12 @@ def moe_expert_down_q8_int8ret(slot_count, slot_offset, slot_logical, w_down, s_
                                             _ptr(scratch), scratch.numel() * scratch.element_size(),
                                             _stream(stream)),
            "moe_expert_down_q8_int8ret")
+
+
+def moe_router_logits(x, w_router, g: Geom, logits, scratch, stream=None):
+    _check(lib().moe_router_logits(_ptr(x), _ptr(w_router), ctypes.byref(g), _ptr(logits),
+                                   _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                   _stream(stream)), "moe_router_logits")
 
 
 def moe_relay_returns(ret, phys_ids, slot_partition, ret_row, g: Geom, comb_row, stream=None):

@@ -14,6 +14,19 @@ inline int64_t msg_bytes_of(const moe_geom_t &g) {
   return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 127) / 128) * 128;
 }
 inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
+// K splits of the router GEMM (bf16 [T][H] x [E][H]^T): 4 when the 128-row x
+// 256-expert tiles alone fill the GPU, more for small T (up to 32, and at
+// least one 64-byte K step per split); 0 = H not a multiple of 32.
+inline int router_splits(const moe_geom_t &g) {
+  const int64_t tiles = (((int64_t)g.T + 127) / 128) * ((g.E + 255) / 256);
+  int ks = 4;
+  while (ks < 32 && tiles * ks < 256) ks *= 2;
+  while (ks > 1 && g.H % (32 * ks) != 0) ks /= 2;
+  return g.H % 32 == 0 ? ks : 0;
+}
+inline int64_t router_scratch_bytes_of(const moe_geom_t &g) {
+  return (int64_t)router_splits(g) * g.T * g.E * 4;
+}
 // INT8 return row: H codes, then one fp32 scale per MOE_RET_Q8_BLOCK columns, 16-byte rows
 inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
   const int64_t nblk = ((int64_t)g.H + MOE_RET_Q8_BLOCK - 1) / MOE_RET_Q8_BLOCK;

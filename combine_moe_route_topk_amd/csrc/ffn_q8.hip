@@ -24,6 +24,8 @@
 // n-tiles, then m inside the group, and blocks are remapped so that each XCD
 // walks one contiguous stretch of it: the m-tiles of a group share every
 // weight tile in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -31,6 +33,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BN = 256, BK = 64;
 #define MOE_LDS __attribute__((address_space(3)))
@@ -50,7 +54,11 @@ static_assert(128 * kStageStride * 4 <= kStages * (BM + BN) * BK, "staging fits 
 static_assert(128 * kStageStrideB <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
 constexpr int kXcds = 8;
 
-enum Mode { GATEUP = 0, DOWN = 1 };
+// GATEUP, DOWN: the INT8 expert projections.  ROUTER: the gate's bf16 logits
+// x . W_router^T (bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation); a
+// 32-byte K sub-step holds 16 bf16 elements, so the operand movement and
+// layout are the same as for INT8.
+enum Mode { GATEUP = 0, DOWN = 1, ROUTER = 2 };
 
 // ------------------------------------------------------------------ prep ---
 __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restrict__ slot_count,
@@ -146,20 +154,43 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   auto lds_b = [&](int st) { return lds + kStages * BM * LDS_STRIDE + st * BN * LDS_STRIDE; };
   __shared__ float row_scale[BM];
 
-  const int K = MODE == GATEUP ? H : I;
+  // ROUTER reuses the arguments: disp_buf = x (bf16 [nrows][H]), w = W_router
+  // (bf16 [E][H]), P = number of K splits, h_out = partial logits
+  // [P][nrows][E] (fp32); its K is the byte length of one split.
+  const int K = MODE == GATEUP ? H : MODE == DOWN ? I : 2 * H / P;
   const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
   Tile tl;
-  if (!decode_tile(tiles, slot_count, P, NT, tl)) return;
-  const int e = slot_logical[tl.p];
-  if (e < 0 || e >= E) return;
-  const int cnt = slot_count[tl.p];
-  const int64_t row0 = (int64_t)slot_offset[tl.p] + (int64_t)tl.m * BM;  // first dense row
-  const int rows_here = min(BM, cnt - tl.m * BM);
+  int e = 0, rows_here = 0, ksplit = 0;
+  int64_t row0 = 0;
+  if constexpr (MODE == ROUTER) {
+    // tiles ordered (split, n-tile, m-tile) so that the blocks of one XCD
+    // stretch share one split's slice of W_router in their L2
+    const int MT = (int)((nrows + BM - 1) / BM), NTR = (E + BN - 1) / BN;
+    const int64_t total = (int64_t)MT * NTR * P;
+    const int64_t per = (total + kXcds - 1) / kXcds;
+    const int64_t i = blockIdx.x / kXcds;
+    if (i >= per) return;
+    const int64_t L = (blockIdx.x % kXcds) * per + i;
+    if (L >= total) return;
+    tl.p = 0;
+    tl.m = (int)(L % MT);
+    tl.n = (int)((L / MT) % NTR);
+    ksplit = (int)(L / ((int64_t)MT * NTR));
+    row0 = (int64_t)tl.m * BM;
+    rows_here = (int)min((int64_t)BM, nrows - row0);
+  } else {
+    if (!decode_tile(tiles, slot_count, P, NT, tl)) return;
+    e = slot_logical[tl.p];
+    if (e < 0 || e >= E) return;
+    const int cnt = slot_count[tl.p];
+    row0 = (int64_t)slot_offset[tl.p] + (int64_t)tl.m * BM;  // first dense row
+    rows_here = min(BM, cnt - tl.m * BM);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // per-row scale of this tile (activation scale s_x, or hs)
-  if (tid < BM) {
+  if (MODE != ROUTER && tid < BM) {
     float sc = 0.0f;
     const int64_t rr = row0 + tid;
     if (tid < rows_here && rr < nrows) {
@@ -191,6 +222,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       const int32_t dr = slot_rows[rr];
       return disp_buf + (int64_t)(dr >= 0 ? dr : 0) * msg + c;
     }
+    if (MODE == ROUTER) return disp_buf + rr * 2 * H + (int64_t)ksplit * K + c;
     return (const uint8_t *)hq + rr * I + c;
   };
   auto b_row_ptr = [&](int r) -> const uint8_t * {
@@ -200,6 +232,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       const int wrow = r < BN / 2 ? n : I + n;
       return (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + c;
     }
+    if (MODE == ROUTER)
+      return (const uint8_t *)w + (int64_t)min(tl.n * BN + r, E - 1) * 2 * H + (int64_t)ksplit * K + c;
     const int wrow = min(tl.n * BN + r, H - 1);
     return (const uint8_t *)w + ((int64_t)e * H + wrow) * I + c;
   };
@@ -222,7 +256,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   const int nbo0 = MODE == GATEUP ? wave * 32 : wave * 64;
   const int nbo1 = MODE == GATEUP ? BN / 2 + wave * 32 : wave * 64 + 32;
 
-  v16i acc[MB][NB];
+  using AccT = std::conditional_t<MODE == ROUTER, v16f, v16i>;
+  AccT acc[MB][NB];
 #pragma unroll
   for (int a = 0; a < MB; ++a)
 #pragma unroll
@@ -272,8 +307,14 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (mb >= mb_live) break;  // 32-row blocks past the slot's rows: nothing to compute
-        acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
+        if constexpr (MODE == ROUTER) {
+          const v8bf a = __builtin_bit_cast(v8bf, af[ks][mb]);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][0]), acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][1]), acc[mb][1], 0, 0, 0);
+        } else {
+          acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
+        }
       }
     }
   }
@@ -287,6 +328,24 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // padded so the two lane halves hit different banks) and leave as 16-byte
   // vector stores.
   const int col = lane & 31, half = lane >> 5;
+  if constexpr (MODE == ROUTER) {
+    // partial logits of this K split: acc[mb][nb][r] is tile row
+    // mb*32 + 8*(r/4) + 4*half + r%4, column wave*64 + nb*32 + col; a half
+    // wave stores 32 consecutive fp32 (one 128-byte line) per register
+    float *part = h_out + (int64_t)ksplit * nrows * E;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = tl.n * BN + wave * 64 + nb * 32 + col;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (lr < rows_here && c < E) part[(row0 + lr) * E + c] = acc[mb][nb][r];
+        }
+    }
+    return;
+  } else {
   float *stg = (float *)lds;
   auto stage_put = [&](int lr, int sc, float v) { stg[lr * kStageStride + sc] = v; };
   if (MODE == GATEUP) {
@@ -423,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
             *(const uint4 *)((const uint8_t *)stb + lr * kStageStrideB + c8 * 2);
     }
   }
+  }  // MODE != ROUTER
 }
 
 // ---------------------------------------------------------------- requant ---
@@ -478,6 +538,25 @@ __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restric
     if (c < n4) dst[c] = code4(v[q]);
   }
   for (int c = kRequantMaxI / 4 + lane; c < n4; c += 64) dst[c] = code4(src[c]);
+}
+
+// ------------------------------------------------------- router reduce ---
+// logits = sum of the K-split partial logits, in split order (fixed, so the
+// result does not depend on scheduling); n = T * E, a multiple of 4.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restrict__ part,
+                                                            int64_t n, int splits,
+                                                            float *__restrict__ logits) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 a = *(const float4 *)(part + i);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 b = *(const float4 *)(part + (int64_t)sp * n + i);
+    a.x = a.x + b.x;
+    a.y = a.y + b.y;
+    a.z = a.z + b.z;
+    a.w = a.w + b.w;
+  }
+  *(float4 *)(logits + i) = a;
 }
 
 }  // namespace
@@ -632,4 +711,34 @@ extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count
   if (st != MOE_OK) return st;
   return moe_expert_down_q8(slot_count, slot_offset, slot_logical, w_down, s_down, I, g, ret,
                             acc_down_dbg, scratch, scratch_bytes, stream);
+}
+
+extern "C" int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g,
+                                 float *logits, void *scratch, size_t scratch_bytes,
+                                 void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  const int ks = router_splits(*g);
+  if (ks == 0 || g->E % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (g->T == 0) return MOE_OK;
+  if (!x || !w_router || !logits || !scratch) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) || !aligned16(scratch))
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)scratch_bytes < router_scratch_bytes_of(*g)) return MOE_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t mt = ((int64_t)g->T + BM - 1) / BM, nt = (g->E + BN - 1) / BN;
+  const int64_t blocks = (mt * nt * ks + kXcds - 1) / kXcds * kXcds;
+  float *part = (float *)scratch;
+  hipLaunchKernelGGL((ffn_gemm_kernel<ROUTER, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const int32_t *)nullptr, (const int32_t *)nullptr, (const int32_t *)nullptr,
+                     (const int32_t *)nullptr, (const int32_t *)nullptr, (const uint8_t *)x,
+                     (int64_t)0, (const int8_t *)nullptr, (const float *)nullptr,
+                     (const int8_t *)w_router, (const float *)nullptr, ks, g->E, g->H, 0,
+                     (int64_t)g->T, part, (float *)nullptr, (uint16_t *)nullptr, (int64_t)0,
+                     (int32_t *)nullptr);
+  if ((st = launch_status()) != MOE_OK) return st;
+  const int64_t n = (int64_t)g->T * g->E;
+  hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                     part, n, ks, logits);
+  return launch_status();
 }

@@ -84,6 +84,7 @@ extern "C" int moe_plan_sizes(const moe_geom_t *g, int32_t I, moe_sizes_t *out) 
   out->combine_bytes_per_partition = (int64_t)g->D * cap * g->H * 2;
   out->relay_bytes = g->relays ? (int64_t)(g->D - g->relays) * g->S * cap * msg : 0;
   out->return_bytes = (int64_t)g->T * g->k * g->H * 2 * (g->relays ? 2 : 1);
+  out->router_scratch_bytes = router_scratch_bytes_of(*g);
   out->ret_q8_row_bytes = ret_q8_row_bytes_of(*g);
   out->ret_q8_bytes = (int64_t)g->T * g->k * out->ret_q8_row_bytes;
   out->dispatch_scratch_bytes = dispatch_scratch_layout(*g).total;

@@ -16,7 +16,7 @@ import torch
 from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16, RET_Q8_BLOCKS,
                RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_down_q8,
                moe_expert_down_q8_int8ret, moe_expert_ffn_q8, moe_expert_gateup_q8,
-               moe_plan_sizes, moe_relay_returns, moe_route_topk)
+               moe_plan_sizes, moe_relay_returns, moe_route_topk, moe_router_logits)
 
 
 class MoeBuffers:
@@ -47,6 +47,15 @@ class MoeBuffers:
         self.ret = torch.empty((nret, H), dtype=torch.int16, device=device)
         self.comb_row = torch.empty((T, k), **i32) if g.relays else None
         self.out = torch.empty((T, H), dtype=out_dtype, device=device)
+
+    def router_buffers(self):
+        """fp32 gate logits [T][E] and the router's split-K scratch (allocated on first use)."""
+        if getattr(self, "_logits32", None) is None:
+            dev = self.out.device
+            self._logits32 = torch.empty((self.g.T, self.g.E), dtype=torch.float32, device=dev)
+            self._rscratch = torch.empty(max(self.sizes.router_scratch_bytes, 256),
+                                         dtype=torch.uint8, device=dev)
+        return self._logits32, self._rscratch
 
     def ret_q8_rows(self):
         """INT8 expert return rows [T*k][ret_q8_row_bytes] bytes (allocated on first use)."""
@@ -86,6 +95,13 @@ class MoeLayer:
     @staticmethod
     def _dt(t: torch.Tensor) -> int:
         return DTYPE_BF16 if t.dtype in (torch.bfloat16, torch.int16, torch.uint16) else DTYPE_F32
+
+    def router(self, x, w_router):
+        """Gate logits from the hidden states: x [T][H] bf16, w_router [E][H] bf16 ->
+        fp32 logits [T][E] (returned; route() takes them)."""
+        logits, scratch = self.buf.router_buffers()
+        moe_router_logits(x, w_router, self.g, logits, scratch)
+        return logits
 
     def route(self, logits):
         b = self.buf

@@ -125,6 +125,7 @@ typedef struct moe_sizes {
   int64_t ffn_scratch_bytes;           /* scratch of moe_expert_ffn_q8 (I > 0)            */
   int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256), 16B   */
   int64_t ret_q8_bytes;                /* T * k INT8 return rows                          */
+  int64_t router_scratch_bytes;        /* scratch of moe_router_logits                    */
 } moe_sizes_t;
 
 /*
@@ -179,6 +180,26 @@ int moe_route_topk(const void *logits, moe_dtype_t logits_dtype, const float *bi
                    moe_gating_t gating, const int32_t *replica_offsets,
                    const int32_t *replica_slots, const moe_geom_t *g, int32_t *topk_ids,
                    float *topk_w, int32_t *phys_ids, int32_t *expert_counts, void *stream);
+
+/*
+ * moe_router_logits -- the gate's logits from the hidden states [CMI EP320
+ * fused_moe listing: gate.topk(hidden, k = 8) opens the MoE step; CMI
+ * "INT8：少搬一些": gating stays in BF16/FP32 while the matmuls go INT8; XDS
+ * P038: dispatch and combine follow the gating scores]:
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h]
+ * bf16 operands, products and sums in fp32 (MFMA), fp32 logits.  The sum over
+ * h is split into router_splits parts whose partial sums are added in split
+ * order, so the result is the same every run; its error against the exact
+ * value is within the fp32 summation bound (H * 2^-24 * sum |x w|).  Feed
+ * the logits to moe_route_topk (MOE_DTYPE_F32).
+ *   x        [T][H] bf16, 16B;  w_router [E][H] bf16, 16B;  H % 32 == 0, E % 4 == 0
+ *   logits   [T][E] fp32, 16B
+ *   scratch  router_scratch_bytes (moe_plan_sizes), 16B
+ * Errors: MOE_ERR_UNSUPPORTED (H % 32 or E % 4), MOE_ERR_CAPACITY (scratch),
+ * MOE_ERR_INVALID_ARG (NULL or misaligned pointers).
+ */
+int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g, float *logits,
+                      void *scratch, size_t scratch_bytes, void *stream);
 
 /*
  * moe_dispatch_q8 -- token-wise INT8 quantization fused into the scatter into

@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 # stream ids (first element of the spawn key)
-S_LOGITS, S_BIAS, S_X, S_RETURNS, S_WEIGHTS, S_SCALES, S_CALIB = range(7)
+S_LOGITS, S_BIAS, S_X, S_RETURNS, S_WEIGHTS, S_SCALES, S_CALIB, S_ROUTER = range(8)
 
 _THREADS = 8
 
@@ -133,6 +133,13 @@ def logits(w: Workload, calib_slice: Optional[int] = None) -> np.ndarray:
         return _normal_rows(w, S_LOGITS, w.T, w.E, w.logits_dtype)
     v = _rng(w, S_CALIB, calib_slice).standard_normal((w.calib_tokens, w.E), dtype=np.float32)
     return to_bf16_bits(v) if w.logits_dtype == "bf16" else v
+
+
+def router_weights(w: Workload) -> np.ndarray:
+    """Gate weights [E][H] as bf16 bit patterns, N(0, 1/H), so that N(0,1) hidden
+    states give logits of unit variance."""
+    v = _rng(w, S_ROUTER).standard_normal((w.E, w.H), dtype=np.float32) / np.float32(np.sqrt(w.H))
+    return to_bf16_bits(v)
 
 
 def zipf_bias(w: Workload) -> Optional[np.ndarray]:

@@ -126,6 +126,52 @@ def _check_dispatch(c: Case, phys, row_sample=None):
     return q, s, lay
 
 
+# ----------------------------------------------------------- gate logits ---
+
+def _router_case(w, token_sample=None):
+    """GPU gate logits of the workload's hidden states against the exact oracle,
+    within the fp32 summation bound H * 2^-24 * sum |x w| (any order of fp32
+    sums of the exact bf16 products stays inside it)."""
+    c = Case(w)
+    wr = mw.router_weights(w)
+    logits = c.layer.router(c.x_d, dev_bits(wr, True))
+    torch.cuda.synchronize()
+    got = host(logits)
+    rows = np.arange(w.T) if token_sample is None else token_sample
+    ref = oracle.router_logits(np.ascontiguousarray(c.x[rows]), wr)
+    mag = oracle.router_logits(np.ascontiguousarray(c.x[rows]) & np.uint16(0x7FFF),
+                               wr & np.uint16(0x7FFF))
+    err = np.abs(got[rows].astype(np.float64) - ref)
+    bound = w.H * 2.0 ** -24 * mag + 1e-30
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    return c, got
+
+
+@pytest.mark.parametrize("name", ["ragged", "decode96"])
+def test_router_logits_and_topk(name):
+    """Gate logits (bf16 MFMA, split-K, fixed-order reduction) within the fp32
+    bound of the exact values; the top-k of the GPU's own fp32 logits is the
+    oracle's top-k of the same logits bit for bit, and two runs give the same
+    bits.  ragged: T = 300 (a partial 128-row tile), E = 40 (a partial expert
+    tile); decode96: T = 96, 32 K splits."""
+    w = RAGGED if name == "ragged" else mw.WORKLOADS["decode96"]
+    c, got = _router_case(w)
+    again = host(c.layer.router(c.x_d, dev_bits(mw.router_weights(w), True)))
+    assert np.array_equal(got, again), "deterministic"
+    c.layer.route(to_dev(got))
+    ids, sc, tw = oracle.route_topk(got, w.k, w.gating, c.bias, logits_bf16=False)
+    b = c.layer.buf
+    assert np.array_equal(host(b.topk_ids), ids), "top-k of the GPU logits"
+    assert_close(host(b.topk_w), tw, FP32_RTOL, FP32_ATOL, "top-k weights")
+
+
+def test_router_logits_layer12288_sampled_tokens():
+    """The gate at the headline shape (T = 12288, H = 7168, E = 256): 96 sampled
+    tokens' logits within the fp32 bound of the exact values."""
+    rng = np.random.default_rng(5)
+    _router_case(mw.WORKLOADS["layer12288"], np.sort(rng.choice(12288, 96, replace=False)))
+
+
 # ------------------------------------------------------------------ route ---
 
 @pytest.mark.parametrize("name", ["tiny", "decode96", "global12288", "eplb4096", "twohop46080"])
