@@ -130,6 +130,31 @@ def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
     return total_ms / steps, per, dist
 
 
+def time_pipeline(layer, x, lg, w, steps, warmup, n_micro=2):
+    """Whole steps of the same layer as a pipeline of n_micro microbatches (source
+    partition groups), each on its own stream."""
+    import torch
+    import combine_moe_route_topk_amd as moe
+    pipe = moe.MoePipeline(layer.g, n_micro, w.gating, layer.slot_partition, layer.slot_logical,
+                           None, None, layer.bias, layer.weights, w.I, torch.bfloat16)
+    for _ in range(warmup):
+        pipe.forward(x, lg)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        pipe.forward(x, lg)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del pipe
+    torch.cuda.empty_cache()
+    return {"n_micro": n_micro, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "note": "route + dispatch + experts + combine per microbatch on its own stream; "
+                    "the output equals the one-batch step's bit for bit"}
+
+
 def time_router(layer, x, w, steps, warmup):
     """moe_router_logits on the layer's hidden states: x [T][H] . W_router^T -> fp32 [T][E]."""
     import numpy as np
@@ -392,6 +417,9 @@ def main():
                              "bytes": dc8_bytes, "us": round(dc8_ms * 1e3, 2)},
         "note": "expert returns quantized to INT8 in the down projection's epilogue (one "
                 "fp32 scale per 256 columns); not the headline configuration (bf16 returns)"}
+    # the microbatch pipeline: two halves of the sources on two streams
+    result["microbatch_pipeline"] = time_pipeline(layer, x, lg, w, args.steps, args.warmup)
+    log(f"[bench] 2-microbatch pipeline: {result['microbatch_pipeline']['ms_per_step']:.3f} ms/step")
     # the gate's logits from the hidden states (bf16 MFMA, split-K), timed alone:
     # the headline step starts from the logits, as the workload defines
     result["router"] = time_router(layer, x, w, args.steps, args.warmup)

@@ -235,4 +235,4 @@ def moe_combine(mode: int, src, row, topk_w, g: Geom, out_dtype: int, out, strea
                              _ptr(out), _stream(stream)), "moe_combine")
 
 
-from .layer import MoeBuffers, MoeLayer  # noqa: E402,F401
+from .layer import MoeBuffers, MoeLayer, MoePipeline  # noqa: E402,F401

@@ -170,3 +170,54 @@ class MoeLayer:
                 self.experts()
         self.combine(combine)
         return self.buf.out
+
+
+class MoePipeline:
+    """A microbatch pipeline of one MoE layer on one GPU [XDS, the microbatch
+    overlap of communication with computation (P108-P111); CMI, the microbatch
+    section].  The batch is split by source partitions into n microbatches,
+    each with its own static buffers and its own (default-priority) stream, so
+    one microbatch's route and dispatch can run while another is in its
+    experts.  Every token's result is independent of the split (routes,
+    replica rotation by batch position, quantization, expert rows and the
+    combine are per token), so the output equals MoeLayer.forward's bit for
+    bit.  Orchestration only: every step runs in the library's kernels."""
+
+    def __init__(self, g: Geom, n_micro: int, gating: str, slot_partition: torch.Tensor,
+                 slot_logical: torch.Tensor, replica_offsets: Optional[torch.Tensor] = None,
+                 replica_slots: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                 weights=None, I: int = 0, out_dtype: torch.dtype = torch.bfloat16):
+        if n_micro < 1 or g.S % n_micro:
+            raise ValueError("the source partitions must split evenly into microbatches")
+        if g.relays:
+            raise ValueError("the two-hop geometry is not pipelined")
+        self.n = n_micro
+        sub = Geom(g.T // n_micro, g.H, g.E, g.P, g.k, g.D, g.Epp, g.S // n_micro, g.LB,
+                   g.msg_bytes, 0, 0)
+        self.tm = sub.T
+        self.layers = [MoeLayer(sub, gating, slot_partition, slot_logical, replica_offsets,
+                                replica_slots, bias, weights, I, out_dtype)
+                       for _ in range(n_micro)]
+        self.streams = [torch.cuda.Stream() for _ in range(n_micro)]
+        self.out = torch.empty((g.T, g.H), dtype=out_dtype, device=slot_partition.device)
+        for i, layer in enumerate(self.layers):
+            layer.buf.out = self.out[i * sub.T:(i + 1) * sub.T]
+
+    def forward(self, x, logits, combine: str = "bf16"):
+        """route -> dispatch -> experts -> combine of each microbatch on its stream;
+        the caller's stream waits for all of them."""
+        cur = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(cur)
+        done = []
+        for i, (layer, s) in enumerate(zip(self.layers, self.streams)):
+            s.wait_event(start)
+            with torch.cuda.stream(s):
+                layer.forward(x[i * self.tm:(i + 1) * self.tm], logits[i * self.tm:(i + 1) * self.tm],
+                              combine)
+            ev = torch.cuda.Event()
+            ev.record(s)
+            done.append(ev)
+        for ev in done:
+            cur.wait_event(ev)
+        return self.out

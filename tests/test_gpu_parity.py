@@ -501,6 +501,30 @@ def test_layer_int8_returns_small_end_to_end():
     assert_close(bf16_to_f32(out), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL, "layer output")
 
 
+@pytest.mark.parametrize("name,n_micro", [("ffn_small", 2), ("ragged", 3)])
+def test_microbatch_pipeline_equals_one_batch(name, n_micro):
+    """The microbatch pipeline (one microbatch per source partition group, each
+    on its own stream) gives the single-batch layer's output bit for bit, twice
+    in a row; ffn_small runs the INT8 SwiGLU experts, ragged identity experts
+    with the INT8 combine."""
+    w = FFN_SMALL if name == "ffn_small" else RAGGED
+    if w.experts == "swiglu":
+        c, _, _, weights = _ffn_case(w)
+        mode = "bf16"
+    else:
+        c = Case(w)
+        mode = "q8"
+    ref = c.layer.forward(c.x_d, c.lg_d, combine=mode).clone()
+    pipe = moe.MoePipeline(c.g, n_micro, w.gating, to_dev(c.sp), to_dev(c.sl), None, None,
+                           None if c.bias is None else to_dev(c.bias), c.layer.weights, w.I,
+                           c.layer.out_dtype)
+    for _ in range(2):
+        out = pipe.forward(c.x_d, c.lg_d, combine=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
+
+
 def test_expert_ffn_layer12288_sampled_rows():
     """The headline layer (T=12288, 256 experts, I=2048, Zipf routing), launched as
     the bench launches it; the oracle recomputes 32 rows of each of four slots
