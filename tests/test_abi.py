@@ -93,6 +93,39 @@ def test_invalid_arguments_rejected_before_launch():
         moe.moe_plan_sizes(bad)
 
 
+def test_int8_returns_and_router_validation():
+    """The INT8-return and gate-logit entry points check their arguments on the
+    host and return an error code without launching (runs without a GPU)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    g = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    s = moe.moe_plan_sizes(g, 256)
+    # INT8 return rows: H codes + one fp32 scale per 256 columns, 16-byte rows
+    assert s.ret_q8_row_bytes == 256 + 16 and s.ret_q8_bytes == 16 * 2 * 272
+    relay = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=1, S=4, LB=4, relays=2)
+    assert L.moe_expert_down_q8_int8ret(fake, fake, fake, fake, fake, 256, ctypes.byref(relay),
+                                        fake, None, fake, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down_q8_int8ret(None, fake, fake, fake, fake, 256, ctypes.byref(g), fake,
+                                        None, fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    # combine: an unknown return mode
+    assert L.moe_combine(3, fake, fake, fake, ctypes.byref(g), 0, fake, None) == moe.MOE_ERR_INVALID_ARG
+    # router: H a multiple of 32, E a multiple of 4, scratch large enough, 16-byte alignment
+    odd_h = moe.geom(T=16, H=80, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    assert L.moe_router_logits(fake, fake, ctypes.byref(odd_h), fake, fake, 1 << 30,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    odd_e = moe.geom(T=16, H=256, E=6, P=6, k=2, D=3, Epp=2, S=4, LB=4)
+    assert L.moe_router_logits(fake, fake, ctypes.byref(odd_e), fake, fake, 1 << 30,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_router_logits(fake, fake, ctypes.byref(g), fake, fake,
+                               s.router_scratch_bytes - 1, None) == moe.MOE_ERR_CAPACITY
+    assert L.moe_router_logits(ctypes.c_void_p(0x1008), fake, ctypes.byref(g), fake, fake,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    # split count: whole 64-byte K steps per split, more splits for few tokens
+    assert s.router_scratch_bytes % (16 * 8 * 4) == 0
+    splits = s.router_scratch_bytes // (16 * 8 * 4)
+    assert 4 <= splits <= 32 and (2 * 256) % (64 * splits) == 0
+
+
 @pytest.mark.parametrize("seed,E,slices,budget", [(0, 32, 4, 8), (1, 64, 3, 16), (2, 8, 1, 5)])
 def test_eplb_planner_matches_oracle(seed, E, slices, budget):
     rng = np.random.default_rng(seed)
