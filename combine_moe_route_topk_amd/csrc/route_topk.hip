@@ -4,106 +4,185 @@
 //  P078-P079 / Fig. 12 (logical -> physical gather, round robin by position)]
 //
 // One 64-lane wavefront per token: lane l holds the scores of experts
-// l*EPL .. l*EPL+EPL-1.  Each score is packed with its id into a 64-bit key
-// that orders by (score descending, id ascending); k rounds of a wavefront
-// max-reduction pick the routes in order, so ties resolve to the lower id
-// exactly as a stable sort would, with no fp comparison subtleties.
+// l*EPL .. l*EPL+EPL-1 as 32-bit order keys (unsigned order = float order).
+// The k-th largest key is found by a radix select over its 32 bits, one bit
+// per round, where each round's count is the popcount of the wavefront's
+// ballots: scalar work, no cross-lane data movement.  The select stops as soon
+// as exactly k keys reach the threshold; otherwise the threshold is the k-th
+// largest key itself and the keys equal to it are taken lowest expert id
+// first.  The k chosen keys are then read out with readlane into lanes
+// 0..k-1, each lane counting the chosen keys that outrank its own (score
+// descending, id ascending), so lane j ends up knowing its route's rank.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kWaves = 4;          // wavefronts per block
-constexpr int kTokensPerWave = 4;  // tokens each wavefront handles in turn
+constexpr int kBlock = 1024;      // threads per block (16 wavefronts)
+constexpr int kMaxBlocks = 256;   // one block per CU: bounds the histogram's global atomics
 
-__device__ __forceinline__ uint64_t make_key(float s, int e) {
+__device__ __forceinline__ uint32_t order_key(float s) {
   if (s == 0.0f) s = 0.0f;  // -0 and +0 are the same score
-  uint32_t u = __float_as_uint(s);
-  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_score(uint64_t key) {
-  uint32_t ord = (uint32_t)(key >> 32);
-  uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
-  return __uint_as_float(u);
+__device__ __forceinline__ float key_score(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
 }
-__device__ __forceinline__ int key_id(uint64_t key) { return (int)(~(uint32_t)key); }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+__device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
 
 __global__ void zero_i32(int32_t *p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 
-template <int EPL, bool BF16>
-__global__ __launch_bounds__(64 * kWaves) void route_topk_kernel(
+// Loads the EPL raw logits of one lane (FULL: E == 64*EPL, so the lane's
+// run is whole and aligned to its size and can go as one vector load).
+template <int EPL, bool BF16, bool FULL>
+__device__ __forceinline__ void load_row(const void *logits, int64_t t, int E, int lane,
+                                         float (&v)[EPL]) {
+  if constexpr (BF16) {
+    const uint16_t *row = (const uint16_t *)logits + t * E + lane * EPL;
+    if constexpr (FULL) {
+      constexpr int kAlign = EPL * 2 >= 16 ? 16 : EPL * 2;
+      const uint16_t *p = (const uint16_t *)__builtin_assume_aligned(row, kAlign);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i] = bf16_bits_to_f32(__builtin_nontemporal_load(p + i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        v[i] = lane * EPL + i < E ? bf16_bits_to_f32(__builtin_nontemporal_load(row + i)) : 0.0f;
+    }
+  } else {
+    const float *row = (const float *)logits + t * E + lane * EPL;
+    if constexpr (FULL) {
+      constexpr int kAlign = EPL * 4 >= 16 ? 16 : EPL * 4;
+      const float *p = (const float *)__builtin_assume_aligned(row, kAlign);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i] = __builtin_nontemporal_load(p + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        v[i] = lane * EPL + i < E ? __builtin_nontemporal_load(row + i) : 0.0f;
+    }
+  }
+}
+
+template <int EPL, bool BF16, bool FULL>
+__global__ __launch_bounds__(kBlock) void route_topk_kernel(
     const void *__restrict__ logits, const float *__restrict__ bias, int gating,
     const int32_t *__restrict__ roff, const int32_t *__restrict__ rslots, int T, int E, int P,
     int k, int LB, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
     int32_t *__restrict__ phys_ids, int32_t *__restrict__ expert_counts) {
   extern __shared__ int32_t hist[];  // [E] when expert_counts != nullptr
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   if (expert_counts) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
   }
-  const int64_t t_base = ((int64_t)blockIdx.x * kWaves + wave) * kTokensPerWave;
-  for (int it = 0; it < kTokensPerWave; ++it) {
-    const int64_t t = t_base + it;
-    if (t >= T) break;
-    uint64_t key[EPL];
+  float bv[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane * EPL + i;
-      key[i] = 0;  // below every real score key
-      if (e < E) {
-        float v = BF16 ? bf16_bits_to_f32(((const uint16_t *)logits)[t * E + e])
-                       : ((const float *)logits)[t * E + e];
-        float b = bias ? bias[e] : 0.0f;
-        key[i] = make_key(v + b, e);
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    bv[i] = bias && e < E ? bias[e] : 0.0f;
+  }
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  // the wavefront index is uniform; saying so keeps the token loop and the
+  // select below on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  float raw[EPL];
+  if (t < T) load_row<EPL, BF16, FULL>(logits, t, E, lane, raw);
+  for (; t < T; t += nwaves) {
+    uint32_t ord[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) ord[i] = lane * EPL + i < E ? order_key(raw[i] + bv[i]) : 0u;
+    if (t + nwaves < T) load_row<EPL, BF16, FULL>(logits, t + nwaves, E, lane, raw);
+
+    // radix select of the k-th largest key (invalid lanes hold 0, below every
+    // candidate, and lose every tie on id)
+    uint32_t tau = 0;
+    int b = 31, c;
+    do {
+      const uint32_t cand = tau | (1u << b);
+      c = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) c += popc64(__ballot(ord[i] >= cand));
+      if (c >= k) tau = cand;
+      --b;
+    } while (b >= 0 && c != k);
+    const bool exact = c == k;
+    uint64_t sel[EPL];
+    if (exact) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) sel[i] = __ballot(ord[i] >= tau);
+    } else {
+      // keys above tau are all chosen; the rest come from the keys equal to
+      // tau in ascending expert id (lane-major, then i)
+      uint64_t eq[EPL];
+      int need = k;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        sel[i] = __ballot(ord[i] > tau);
+        eq[i] = __ballot(ord[i] == tau);
+        need -= popc64(sel[i]);
+      }
+      for (; need > 0; --need) {
+        int best = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (eq[i]) best = min(best, lowest_lane(eq[i]) * EPL + i);
+        const int bl = best / EPL, bi = best % EPL;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (i == bi) {
+            eq[i] &= ~(1ull << bl);
+            sel[i] |= 1ull << bl;
+          }
       }
     }
-    uint64_t mine = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t m = 0;
+
+    // read the k chosen keys out into lanes 0..k-1 and rank them
+    uint32_t my_o = 0;
+    int my_e = 0, rank = 0, j = 0;  // j: keys read out so far
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) m = key[i] > m ? key[i] : m;
-      m = wave_max_u64(m);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (key[i] == m) key[i] = 0;
-      if (lane == j) mine = m;
+    for (int i = 0; i < EPL; ++i) {
+      uint64_t m = sel[i];
+      while (m) {
+        const int l = lowest_lane(m);
+        m &= m - 1;
+        const uint32_t O = (uint32_t)__builtin_amdgcn_readlane((int)ord[i], l);
+        const int Ei = l * EPL + i;
+        const bool older = lane < j;
+        const bool beats = older & ((O > my_o) | ((O == my_o) & (Ei < my_e)));
+        const uint64_t above = __ballot(older & !beats);
+        rank += beats ? 1 : 0;
+        if (lane == j) {
+          my_o = O;
+          my_e = Ei;
+          rank = popc64(above);
+        }
+        ++j;
+      }
     }
-    // lanes 0..k-1 now hold route j = lane
+
+    // lane l < k holds the route of rank `rank`
     const bool act = lane < k;
-    const float s = key_score(mine);
-    const float s0 = __shfl(s, 0, 64);
+    const float s = key_score(my_o);
+    const int l0 = lowest_lane(__ballot(act && rank == 0));
+    const float s0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(s), l0));
     float a = 0.0f;
     if (act) a = gating == MOE_GATING_SOFTMAX ? expf(s - s0) : 1.0f / (1.0f + expf(-s));
-    const float sum = wave_sum_f32(a);
+    float sum = a;
+    for (int o = 1; o < k; o <<= 1) sum += __shfl_xor(sum, o, 64);
     if (act) {
-      const int e = key_id(mine);
-      const int64_t o = t * k + lane;
-      topk_ids[o] = e;
+      const int64_t o = t * k + rank;
+      topk_ids[o] = my_e;
       topk_w[o] = a / sum;
-      int p = e;
+      int p = my_e;
       if (roff) {
-        const int r0 = roff[e], n = roff[e + 1] - r0;
+        const int r0 = roff[my_e], n = roff[my_e + 1] - r0;
         p = -1;
         if (n > 0 && r0 >= 0 && r0 + n <= P) {
           const int b = (int)(t % LB);
@@ -112,33 +191,55 @@ __global__ __launch_bounds__(64 * kWaves) void route_topk_kernel(
         }
       }
       phys_ids[o] = p;
-      if (expert_counts) atomicAdd(&hist[e], 1);
+      if (expert_counts) atomicAdd(&hist[my_e], 1);
     }
   }
   if (expert_counts) {
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-      if (hist[e]) atomicAdd(&expert_counts[e], hist[e]);
+    // Two counters per 64-bit add when the pair is 8-byte aligned: each
+    // counter's total is at most T < 2^31, so the low half never carries.
+    if ((E & 1) == 0 && ((uintptr_t)expert_counts & 7) == 0) {
+      unsigned long long *c2 = (unsigned long long *)expert_counts;
+      for (int e = threadIdx.x; e < E / 2; e += blockDim.x) {
+        const unsigned long long v =
+            (unsigned long long)(uint32_t)hist[2 * e] | ((unsigned long long)(uint32_t)hist[2 * e + 1] << 32);
+        if (v) atomicAdd(c2 + e, v);
+      }
+    } else {
+      for (int e = threadIdx.x; e < E; e += blockDim.x)
+        if (hist[e]) atomicAdd(&expert_counts[e], hist[e]);
+    }
   }
+}
+
+template <int EPL, bool BF16, bool FULL>
+hipError_t launch_route3(const void *logits, const float *bias, int gating, const int32_t *roff,
+                         const int32_t *rslots, const moe_geom_t &g, int32_t *ids, float *w,
+                         int32_t *phys, int32_t *counts, hipStream_t st) {
+  const int waves = kBlock / 64;
+  const int blocks = (int)std::min<int64_t>(((int64_t)g.T + waves - 1) / waves, kMaxBlocks);
+  const size_t lds = counts ? sizeof(int32_t) * g.E : 0;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_topk_kernel<EPL, BF16, FULL>), dim3(blocks), dim3(kBlock), lds, st,
+                     logits, bias, gating, roff, rslots, g.T, g.E, g.P, g.k, g.LB, ids, w, phys,
+                     counts);
+  return hipGetLastError();
 }
 
 template <int EPL>
 hipError_t launch_route(const void *logits, bool bf16, const float *bias, int gating,
                         const int32_t *roff, const int32_t *rslots, const moe_geom_t &g,
                         int32_t *ids, float *w, int32_t *phys, int32_t *counts, hipStream_t st) {
-  const int per_block = kWaves * kTokensPerWave;
-  const int blocks = (g.T + per_block - 1) / per_block;
-  const size_t lds = counts ? sizeof(int32_t) * g.E : 0;
-  if (blocks == 0) return hipSuccess;
+  const bool full = g.E == 64 * EPL;
   if (bf16)
-    hipLaunchKernelGGL((route_topk_kernel<EPL, true>), dim3(blocks), dim3(64 * kWaves), lds, st,
-                       logits, bias, gating, roff, rslots, g.T, g.E, g.P, g.k, g.LB, ids, w, phys,
-                       counts);
-  else
-    hipLaunchKernelGGL((route_topk_kernel<EPL, false>), dim3(blocks), dim3(64 * kWaves), lds, st,
-                       logits, bias, gating, roff, rslots, g.T, g.E, g.P, g.k, g.LB, ids, w, phys,
-                       counts);
-  return hipGetLastError();
+    return full ? launch_route3<EPL, true, true>(logits, bias, gating, roff, rslots, g, ids, w,
+                                                 phys, counts, st)
+                : launch_route3<EPL, true, false>(logits, bias, gating, roff, rslots, g, ids, w,
+                                                  phys, counts, st);
+  return full ? launch_route3<EPL, false, true>(logits, bias, gating, roff, rslots, g, ids, w, phys,
+                                                counts, st)
+              : launch_route3<EPL, false, false>(logits, bias, gating, roff, rslots, g, ids, w,
+                                                 phys, counts, st);
 }
 
 }  // namespace

@@ -180,6 +180,53 @@ def test_route_parity(name):
     _check_route(c)
 
 
+def _selection_scores(rng, T, E, mode):
+    if mode == "ties":      # few distinct values: most boundaries split a run of equal scores
+        return rng.integers(-4, 5, (T, E)).astype(np.float32) * np.float32(0.25)
+    if mode == "equal":     # every score equal: the k lowest ids, in id order
+        return np.full((T, E), 0.5, np.float32)
+    if mode == "zeros":     # +0 and -0 are one score
+        return rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), (T, E))
+    return rng.standard_normal((T, E), dtype=np.float32)
+
+
+@pytest.mark.parametrize("E,k,dtype,mode,biased", [
+    (8, 2, "bf16", "ties", False), (96, 8, "f32", "ties", True), (200, 16, "bf16", "ties", False),
+    (256, 8, "bf16", "equal", False), (256, 8, "f32", "normal", True),
+    (513, 16, "f32", "normal", False), (1024, 16, "bf16", "ties", True),
+    (64, 1, "f32", "zeros", False), (128, 3, "bf16", "normal", True)])
+def test_route_selection_edge_cases(E, k, dtype, mode, biased):
+    """The top-k select on scores built to stress it: a few distinct values
+    (the k-th score is shared by many experts and the lower ids must win), all
+    scores equal, +0 mixed with -0, expert counts that leave the last lanes'
+    runs partial (E = 96, 200, 513) or use every lane (64 .. 1024), both logit
+    dtypes, k from 1 to the maximum 16, with and without a bias.  T = 5000
+    exceeds the capped grid's 4096 wavefronts, so some wavefronts take two
+    tokens.  ids, weights and the expert histogram against the oracle."""
+    T = 5000
+    rng = np.random.default_rng(E * 131 + k)
+    sc = _selection_scores(rng, T, E, mode)
+    lg = mw.to_bf16_bits(sc) if dtype == "bf16" else sc
+    bias = (rng.integers(-8, 9, E).astype(np.float32) * np.float32(0.125)) if biased else None
+    _log(f"[case] route select E={E} k={k} {dtype} {mode} bias={biased}")
+    gating = "softmax" if k % 2 else "sigmoid"
+    g = moe.geom(T, 64, E, E, k, 1, E, 1, T)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    phys = torch.empty_like(ids)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    moe.moe_route_topk(dev_bits(lg, dtype == "bf16"), moe.DTYPE_BF16 if dtype == "bf16" else moe.DTYPE_F32,
+                       None if bias is None else to_dev(bias),
+                       moe.GATING_SOFTMAX if gating == "softmax" else moe.GATING_SIGMOID,
+                       None, None, g, ids, tw, phys, counts)
+    torch.cuda.synchronize()
+    rids, _, rw = oracle.route_topk(lg, k, gating, bias, logits_bf16=dtype == "bf16")
+    assert np.array_equal(host(ids), rids), "topk ids"
+    assert np.array_equal(host(phys), rids), "physical ids without a replica map"
+    assert_close(host(tw), rw, FP32_RTOL, FP32_ATOL, "topk weights")
+    assert np.array_equal(host(counts), oracle.expert_counts(rids, E)), "expert counts"
+
+
 # --------------------------------------------------------------- dispatch ---
 
 @pytest.mark.parametrize("name", ["tiny", "decode96", "ragged"])
