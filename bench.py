@@ -89,9 +89,15 @@ def build_layer(w, log_every=64):
         list(ex.map(fill, range(w.E)))
     torch.cuda.synchronize()
     log(f"[bench] inputs and weights resident in HBM ({time.time() - t0:.1f}s)")
+    # the layer keeps the weights in the expert GEMMs' tile image (packed once,
+    # outside any timed region); the plain copies are released afterwards
     layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
                          torch.from_numpy(sl).cuda(), bias=bias, weights=(wgu, sgu, wd, sd),
                          I=w.I, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    del wgu, wd
+    torch.cuda.empty_cache()
+    log(f"[bench] expert weights packed ({time.time() - t0:.1f}s)")
     return layer, x, lg
 
 

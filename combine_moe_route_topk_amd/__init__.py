@@ -29,11 +29,12 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 GATING_SOFTMAX, GATING_SIGMOID = 0, 1
 RET_Q8_FROM_DISPATCH, RET_BF16, RET_Q8_BLOCKS = 0, 1, 2
 RET_Q8_BLOCK = 256  # columns per scale of the INT8 expert returns
+PROJ_GATEUP, PROJ_DOWN = 0, 1
 
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
-            "moe_status_string")
+            "moe_pack_expert_weights", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -51,7 +52,8 @@ class Sizes(ctypes.Structure):
                 ("msg_bytes", "cap_rows", "dispatch_bytes", "dispatch_bytes_per_partition",
                  "combine_bytes_per_partition", "relay_bytes", "return_bytes",
                  "dispatch_scratch_bytes", "ffn_scratch_bytes", "ret_q8_row_bytes",
-                 "ret_q8_bytes", "router_scratch_bytes")]
+                 "ret_q8_bytes", "router_scratch_bytes", "w_gateup_packed_bytes",
+                 "w_down_packed_bytes")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -89,6 +91,7 @@ def lib():
                                          ctypes.c_size_t, _P]
         L.moe_expert_down_q8_int8ret.argtypes = L.moe_expert_down_q8.argtypes
         L.moe_router_logits.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P, ctypes.c_size_t, _P]
+        L.moe_pack_expert_weights.argtypes = [_P, _I32, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -224,6 +227,12 @@ def moe_router_logits(x, w_router, g: Geom, logits, scratch, stream=None):
                                    _stream(stream)), "moe_router_logits")
 
 
+def moe_pack_expert_weights(w, proj: int, E: int, H: int, I: int, packed, stream=None):
+    _check(lib().moe_pack_expert_weights(_ptr(w), proj, E, H, I, _ptr(packed),
+                                         packed.numel() * packed.element_size(), _stream(stream)),
+           "moe_pack_expert_weights")
+
+
 def moe_relay_returns(ret, phys_ids, slot_partition, ret_row, g: Geom, comb_row, stream=None):
     _check(lib().moe_relay_returns(_ptr(ret), _ptr(phys_ids), _ptr(slot_partition), _ptr(ret_row),
                                    ctypes.byref(g), _ptr(comb_row), _stream(stream)),
@@ -235,4 +244,4 @@ def moe_combine(mode: int, src, row, topk_w, g: Geom, out_dtype: int, out, strea
                              _ptr(out), _stream(stream)), "moe_combine")
 
 
-from .layer import MoeBuffers, MoeLayer, MoePipeline  # noqa: E402,F401
+from .layer import MoeBuffers, MoeLayer, MoePipeline, PackedExpertWeights  # noqa: E402,F401

@@ -9,7 +9,7 @@
 //   prep     per-slot m-tile counts and their prefix (the tile work list).
 //   gateup   grouped GEMM over (slot, m-tile, n-tile): A = the slot's message
 //            rows gathered from the dispatch buffer (int8 codes, K = H),
-//            B = [64 gate rows | 64 up rows] of the slot's logical expert.
+//            B = [128 gate rows | 128 up rows] of the slot's logical expert.
 //            Epilogue: dequantize both, h = silu(g) * u, write h (fp32) and
 //            the per-(row, n-tile) max |h| (no atomics).
 //   requant  per row: amax = max of the partial maxima (exact), token-wise
@@ -20,6 +20,9 @@
 // Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
 // each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes moved global -> LDS by
 // DMA into a ring of three stages, two steps ahead, XOR-swizzled rows.  The
+// weights come pre-packed in the LDS image of each (n-tile, K step) (see
+// moe_pack_expert_weights), so a step's 16 KB of B is one contiguous run of
+// whole cache lines rather than 256 half lines.  The
 // work list is ordered slot-major, then groups of kGroupM m-tiles, then
 // n-tiles, then m inside the group, and blocks are remapped so that each XCD
 // walks one contiguous stretch of it: the m-tiles of a group share every
@@ -209,9 +212,10 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // chunk + 16 i.  Wave w fills A chunks 2w, 2w + 1 and B chunks 4w .. 4w + 3.
   // Lane i covers row 16 q + i / 4 of chunk q and picks the source chunk
   // (i & 3) ^ ((row >> 2) & 3), which produces the swizzled layout above.
-  // Tile rows past the slot's last row, and weight rows past I or H, read a
-  // valid stand-in row instead: they only feed accumulators of rows or
-  // columns that the epilogue never stores.
+  // Tile rows past the slot's last row read a valid stand-in row instead, as
+  // do weight rows past I or H (the packed image holds clamped rows there):
+  // they only feed accumulators of rows or columns that the epilogue never
+  // stores.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane >> 2;
   auto a_row_ptr = [&](int r) -> const uint8_t * {
@@ -225,31 +229,35 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     if (MODE == ROUTER) return disp_buf + rr * 2 * H + (int64_t)ksplit * K + c;
     return (const uint8_t *)hq + rr * I + c;
   };
-  auto b_row_ptr = [&](int r) -> const uint8_t * {
+  auto b_row_ptr = [&](int r) -> const uint8_t * {  // W_router rows (ROUTER only)
     const int c = ((lane & 3) ^ ((r >> 2) & 3)) * 16;
-    if (MODE == GATEUP) {
-      const int n = min(tl.n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);  // gate / up pair index
-      const int wrow = r < BN / 2 ? n : I + n;
-      return (const uint8_t *)w + ((int64_t)e * 2 * I + wrow) * H + c;
-    }
-    if (MODE == ROUTER)
-      return (const uint8_t *)w + (int64_t)min(tl.n * BN + r, E - 1) * 2 * H + (int64_t)ksplit * K + c;
-    const int wrow = min(tl.n * BN + r, H - 1);
-    return (const uint8_t *)w + ((int64_t)e * H + wrow) * I + c;
+    return (const uint8_t *)w + (int64_t)min(tl.n * BN + r, E - 1) * 2 * H + (int64_t)ksplit * K + c;
   };
   const uint8_t *pa0 = a_row_ptr(16 * (2 * wv) + lrow), *pa1 = a_row_ptr(16 * (2 * wv + 1) + lrow);
-  const uint8_t *pb0 = b_row_ptr(16 * (4 * wv) + lrow), *pb1 = b_row_ptr(16 * (4 * wv + 1) + lrow);
-  const uint8_t *pb2 = b_row_ptr(16 * (4 * wv + 2) + lrow), *pb3 = b_row_ptr(16 * (4 * wv + 3) + lrow);
+  // B sources: W_router rows (ROUTER), else this wave's four 1 KB chunks of
+  // the packed weight block of (e, n-tile, K step), lane i at byte 16 i
+  const uint8_t *pb[4];
+  int64_t b_step;
+  if constexpr (MODE == ROUTER) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = b_row_ptr(16 * (4 * wv + c) + lrow);
+    b_step = BK;
+  } else {
+    const uint8_t *blk = (const uint8_t *)w + ((int64_t)e * NT + tl.n) * (K / BK) * kPackedStepBytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = blk + (4 * wv + c) * 1024 + lane * 16;
+    b_step = kPackedStepBytes;
+  }
   auto dma = [&](int kstep, int buf) {
-    const int64_t off = (int64_t)kstep * BK;
+    const int64_t off = (int64_t)kstep * BK, boff = (int64_t)kstep * b_step;
     uint8_t *la = lds_a(buf) + 2 * wv * 1024;
     uint8_t *lb = lds_b(buf) + 4 * wv * 1024;
     __builtin_amdgcn_global_load_lds(pa0 + off, (MOE_LDS void *)(la), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(pa1 + off, (MOE_LDS void *)(la + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb0 + off, (MOE_LDS void *)(lb), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb1 + off, (MOE_LDS void *)(lb + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb2 + off, (MOE_LDS void *)(lb + 2048), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb3 + off, (MOE_LDS void *)(lb + 3072), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb[0] + boff, (MOE_LDS void *)(lb), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb[1] + boff, (MOE_LDS void *)(lb + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb[2] + boff, (MOE_LDS void *)(lb + 2048), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pb[3] + boff, (MOE_LDS void *)(lb + 3072), 16, 0, 0);
   };
 
   // B-tile rows of this wave's two 32-column blocks
@@ -559,6 +567,32 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restr
   *(float4 *)(logits + i) = a;
 }
 
+// ------------------------------------------------------- weight packing ---
+// One thread per 16-byte slot of the image: slot j of tile row r in block
+// (e, n, s) is bytes 64 s + 16 (j ^ ((r >> 2) & 3)) .. +16 of that row's
+// weights -- the swizzled LDS order of the GEMM's K step s.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restrict__ w,
+                                                           int gateup, int E, int H, int I,
+                                                           int8_t *__restrict__ packed) {
+  const int K = gateup ? H : I, KT = K / BK;
+  const int NT = packed_ntiles(gateup ? MOE_PROJ_GATEUP : MOE_PROJ_DOWN, H, I);
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)E * NT * KT * (kPackedStepBytes / 16)) return;
+  const int j = (int)(q & 3), r = (int)((q >> 2) & 255);
+  const int64_t blk = q >> 10;
+  const int s = (int)(blk % KT), n = (int)((blk / KT) % NT);
+  const int64_t e = blk / ((int64_t)KT * NT);
+  const int chunk = j ^ ((r >> 2) & 3);
+  int64_t row;
+  if (gateup) {
+    const int pair = min(n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);
+    row = e * 2 * I + (r < BN / 2 ? pair : I + pair);
+  } else {
+    row = e * H + min(n * BN + r, H - 1);
+  }
+  *(uint4 *)(packed + q * 16) = *(const uint4 *)(w + row * K + (int64_t)s * BK + chunk * 16);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -740,5 +774,23 @@ extern "C" int moe_router_logits(const void *x, const void *w_router, const moe_
   const int64_t n = (int64_t)g->T * g->E;
   hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
                      part, n, ks, logits);
+  return launch_status();
+}
+
+extern "C" int moe_pack_expert_weights(const int8_t *w, moe_proj_t proj, int32_t E, int32_t H,
+                                       int32_t I, int8_t *packed, size_t packed_bytes,
+                                       void *stream) {
+  if (!w || !packed || !aligned16(w) || !aligned16(packed) || E <= 0) return MOE_ERR_INVALID_ARG;
+  if (proj != MOE_PROJ_GATEUP && proj != MOE_PROJ_DOWN) return MOE_ERR_INVALID_ARG;
+  if (H <= 0 || H % 128 != 0 || H > MOE_MAX_H || I <= 0 || I % 64 != 0 || I > 16384)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t bytes = packed_weight_bytes(proj, E, H, I);
+  if ((int64_t)packed_bytes < bytes) return MOE_ERR_CAPACITY;
+  const int64_t w_bytes = (int64_t)E * (proj == MOE_PROJ_GATEUP ? 2 * I : H) * (proj == MOE_PROJ_GATEUP ? H : I);
+  const uintptr_t w0 = (uintptr_t)w, p0 = (uintptr_t)packed;
+  if (w0 < p0 + (uintptr_t)bytes && p0 < w0 + (uintptr_t)w_bytes) return MOE_ERR_INVALID_ARG;
+  const int64_t slots = bytes / 16;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, w, proj == MOE_PROJ_GATEUP ? 1 : 0, E, H, I, packed);
   return launch_status();
 }

@@ -89,6 +89,9 @@ extern "C" int moe_plan_sizes(const moe_geom_t *g, int32_t I, moe_sizes_t *out) 
   out->ret_q8_bytes = (int64_t)g->T * g->k * out->ret_q8_row_bytes;
   out->dispatch_scratch_bytes = dispatch_scratch_layout(*g).total;
   out->ffn_scratch_bytes = I ? ffn_scratch_layout(*g, I).total : 0;
+  const bool ffn = I > 0 && g->H % 128 == 0;
+  out->w_gateup_packed_bytes = ffn ? packed_weight_bytes(MOE_PROJ_GATEUP, g->E, g->H, I) : 0;
+  out->w_down_packed_bytes = ffn ? packed_weight_bytes(MOE_PROJ_DOWN, g->E, g->H, I) : 0;
   return MOE_OK;
 }
 

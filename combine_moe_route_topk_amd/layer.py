@@ -13,10 +13,46 @@ from typing import Optional
 
 import torch
 
-from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, RET_BF16, RET_Q8_BLOCKS,
-               RET_Q8_FROM_DISPATCH, Geom, moe_combine, moe_dispatch_q8, moe_expert_down_q8,
-               moe_expert_down_q8_int8ret, moe_expert_ffn_q8, moe_expert_gateup_q8,
-               moe_plan_sizes, moe_relay_returns, moe_route_topk, moe_router_logits)
+from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, PROJ_DOWN, PROJ_GATEUP,
+               RET_BF16, RET_Q8_BLOCKS, RET_Q8_FROM_DISPATCH, Geom, geom, moe_combine,
+               moe_dispatch_q8, moe_expert_down_q8, moe_expert_down_q8_int8ret, moe_expert_ffn_q8,
+               moe_expert_gateup_q8, moe_pack_expert_weights, moe_plan_sizes, moe_relay_returns,
+               moe_route_topk, moe_router_logits)
+
+
+class PackedExpertWeights:
+    """The routed experts' INT8 SwiGLU weights on the device, each projection in
+    the expert GEMMs' tile image (moe_pack_expert_weights), the fp32 channel
+    scales as given.  Built once from w_gateup [E][2I][H], s_gateup [E][2I],
+    w_down [E][H][I], s_down [E][H] (device tensors, 16-byte aligned); every
+    layer or microbatch that runs these experts shares it.  Iterates as
+    (w_gateup, s_gateup, w_down, s_down) with the packed projections."""
+
+    def __init__(self, w_gateup: torch.Tensor, s_gateup: torch.Tensor, w_down: torch.Tensor,
+                 s_down: torch.Tensor):
+        E, two_i, H = w_gateup.shape
+        I = two_i // 2
+        if tuple(w_down.shape) != (E, H, I) or w_gateup.dtype != torch.int8 \
+                or w_down.dtype != torch.int8:
+            raise ValueError("w_gateup [E][2I][H] and w_down [E][H][I] int8 expected")
+        self.E, self.H, self.I = E, H, I
+        sz = moe_plan_sizes(geom(0, H, E, E, 1, 1, 1, 1, 0), I)
+        dev = w_gateup.device
+        self.w_gateup = torch.empty(sz.w_gateup_packed_bytes, dtype=torch.int8, device=dev)
+        self.w_down = torch.empty(sz.w_down_packed_bytes, dtype=torch.int8, device=dev)
+        moe_pack_expert_weights(w_gateup.contiguous(), PROJ_GATEUP, E, H, I, self.w_gateup)
+        moe_pack_expert_weights(w_down.contiguous(), PROJ_DOWN, E, H, I, self.w_down)
+        self.s_gateup = s_gateup
+        self.s_down = s_down
+
+    def __iter__(self):
+        return iter((self.w_gateup, self.s_gateup, self.w_down, self.s_down))
+
+
+def _packed(weights):
+    if weights is None or isinstance(weights, PackedExpertWeights):
+        return weights
+    return PackedExpertWeights(*weights)
 
 
 class MoeBuffers:
@@ -86,11 +122,21 @@ class MoeLayer:
         self.replica_offsets = replica_offsets
         self.replica_slots = replica_slots
         self.bias = bias
-        self.weights = weights  # (w_gateup, s_gateup, w_down, s_down) device tensors or None
+        self.weights = weights  # PackedExpertWeights, or a plain 4-tuple packed here, or None
         self.I = I
         self.out_dtype = out_dtype
         self.buf = MoeBuffers(g, I, out_dtype)
         self.event_id = 0
+
+    @property
+    def weights(self) -> Optional[PackedExpertWeights]:
+        return self._weights
+
+    @weights.setter
+    def weights(self, w):
+        """A PackedExpertWeights, None, or (w_gateup, s_gateup, w_down, s_down) device
+        tensors in the plain layout, which are packed here (once)."""
+        self._weights = _packed(w)
 
     @staticmethod
     def _dt(t: torch.Tensor) -> int:
@@ -192,6 +238,7 @@ class MoePipeline:
         if g.relays:
             raise ValueError("the two-hop geometry is not pipelined")
         self.n = n_micro
+        weights = _packed(weights)  # one packed copy shared by the microbatches
         sub = Geom(g.T // n_micro, g.H, g.E, g.P, g.k, g.D, g.Epp, g.S // n_micro, g.LB,
                    g.msg_bytes, 0, 0)
         self.tm = sub.T

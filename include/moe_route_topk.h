@@ -76,6 +76,7 @@ enum {
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_GATING_SOFTMAX = 0, MOE_GATING_SIGMOID = 1 } moe_gating_t;
+typedef enum { MOE_PROJ_GATEUP = 0, MOE_PROJ_DOWN = 1 } moe_proj_t;
 typedef enum {
   MOE_RET_Q8_FROM_DISPATCH = 0, /* value rows are dispatch messages (int8 + scale) */
   MOE_RET_BF16 = 1,             /* value rows are bf16 expert returns              */
@@ -126,6 +127,8 @@ typedef struct moe_sizes {
   int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256), 16B   */
   int64_t ret_q8_bytes;                /* T * k INT8 return rows                          */
   int64_t router_scratch_bytes;        /* scratch of moe_router_logits                    */
+  int64_t w_gateup_packed_bytes;       /* moe_pack_expert_weights image, MOE_PROJ_GATEUP  */
+  int64_t w_down_packed_bytes;         /* moe_pack_expert_weights image, MOE_PROJ_DOWN    */
 } moe_sizes_t;
 
 /*
@@ -238,6 +241,31 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
                     void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * moe_pack_expert_weights -- INT8 expert weights into the expert GEMMs' tile
+ * image [XDS DeepSeek INT8 量化, P088: the routed experts' weights are stored
+ * INT8; how they sit in memory is left open].  The image makes the 16 KB of
+ * weights that one 256-row GEMM tile consumes per 64-byte K step one
+ * contiguous run, already in the order the GEMM stages it in LDS, so each
+ * step's weight fetch is whole 128-byte lines.  Run once when the weights are
+ * loaded; the GEMMs take only the image.
+ *   proj MOE_PROJ_GATEUP: w = [E][2I][H] (rows 0..I-1 gate, I..2I-1 up), K = H,
+ *     NT = ceil(I / 128) n-tiles of 128 gate/up pairs; tile row r < 128 is gate
+ *     row min(128 n + r, I - 1), row r >= 128 is up row I + min(128 n + r - 128, I - 1).
+ *   proj MOE_PROJ_DOWN: w = [E][H][I], K = I, NT = ceil(H / 256); tile row r is
+ *     row min(256 n + r, H - 1).
+ *   Image: packed[e][n][s][r][j] for K steps s < K / 64, tile rows r < 256 and
+ *     16-byte slots j < 4: slot j of row r holds bytes 64 s + 16 (j ^ ((r >> 2) & 3))
+ *     .. +16 of that weight row.  Size E * NT * (K / 64) * 16384 bytes
+ *     (w_gateup_packed_bytes / w_down_packed_bytes of moe_plan_sizes).
+ *   Requirements: E > 0, H a multiple of 128, I a multiple of 64 and <= 16384,
+ *     w and packed 16B-aligned and not overlapping, packed_bytes >= the size.
+ * Errors: MOE_ERR_INVALID_ARG (NULL, misaligned, bad proj or E),
+ *   MOE_ERR_UNSUPPORTED (H or I), MOE_ERR_CAPACITY (packed_bytes), MOE_ERR_HIP.
+ */
+int moe_pack_expert_weights(const int8_t *w, moe_proj_t proj, int32_t E, int32_t H, int32_t I,
+                            int8_t *packed, size_t packed_bytes, void *stream);
+
+/*
  * moe_expert_ffn_q8 -- grouped INT8 SwiGLU experts on MFMA
  * [XDS DeepSeek INT8 量化, P085 (QMM: y_ij ~ s_i s^w_j sum_k q(x_ik) q(w_jk), token-wise
  * activation and channel-wise weight scales), P088 (gate and up projections
@@ -252,8 +280,10 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
  *   acc_d = hq . Wd[e][c]                                           (int32, c < H)
  *   ret[slot_offset[p] + i][c] = bf16_rne((f32(acc_d) * hs) * s_down[e][c])
  *   disp_buf   as written by moe_dispatch_q8 (16B)
- *   w_gateup   [E][2I][H] int8 (rows 0..I-1 gate, I..2I-1 up), 16B;  s_gateup [E][2I] fp32
- *   w_down     [E][H][I] int8, 16B;  s_down [E][H] fp32
+ *   w_gateup   Wgu = [E][2I][H] int8 (rows 0..I-1 gate, I..2I-1 up) in the tile image of
+ *              moe_pack_expert_weights (MOE_PROJ_GATEUP), 16B;  s_gateup [E][2I] fp32
+ *   w_down     Wd = [E][H][I] int8 in the tile image of moe_pack_expert_weights
+ *              (MOE_PROJ_DOWN), 16B;  s_down [E][H] fp32
  *   I          multiple of 64, <= 16384 (H a multiple of 128)
  *   ret        [T*k][H] bf16, 16B
  *   acc_gateup_dbg [T*k][2I] int32 or NULL, acc_down_dbg [T*k][H] int32 or NULL:

@@ -126,6 +126,33 @@ def test_int8_returns_and_router_validation():
     assert 4 <= splits <= 32 and (2 * 256) % (64 * splits) == 0
 
 
+def test_pack_expert_weights_validation_and_sizes():
+    """The weight packer's sizes (one 16 KB block per expert, n-tile and 64-byte
+    K step; partial n-tiles padded) and its host-side argument checks (no launch)."""
+    L = moe.lib()
+    s = moe.moe_plan_sizes(moe.geom(T=0, H=7168, E=256, P=256, k=1, D=1, Epp=1, S=1, LB=0), 2048)
+    assert s.w_gateup_packed_bytes == 256 * 2 * 2048 * 7168
+    assert s.w_down_packed_bytes == 256 * 7168 * 2048
+    s = moe.moe_plan_sizes(moe.geom(T=0, H=384, E=3, P=3, k=1, D=1, Epp=1, S=1, LB=0), 192)
+    assert s.w_gateup_packed_bytes == 3 * 2 * (384 // 64) * 16384   # two n-tiles of 128 pairs
+    assert s.w_down_packed_bytes == 3 * 2 * (192 // 64) * 16384     # two n-tiles of 256 rows
+    w, pk = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x40000000)
+    ok = s.w_gateup_packed_bytes
+    G, D = moe.PROJ_GATEUP, moe.PROJ_DOWN
+    assert L.moe_pack_expert_weights(None, G, 3, 384, 192, pk, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(w, G, 3, 384, 192, None, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(ctypes.c_void_p(0x10008), G, 3, 384, 192, pk, ok,
+                                     None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(w, 2, 3, 384, 192, pk, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(w, G, 0, 384, 192, pk, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weights(w, G, 3, 320, 192, pk, ok, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_expert_weights(w, D, 3, 384, 96, pk, ok, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_expert_weights(w, G, 3, 384, 192, pk, ok - 1, None) == moe.MOE_ERR_CAPACITY
+    # the image may not overlap the plain weights
+    assert L.moe_pack_expert_weights(w, G, 3, 384, 192, ctypes.c_void_p(0x10000 + 4096), ok,
+                                     None) == moe.MOE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("seed,E,slices,budget", [(0, 32, 4, 8), (1, 64, 3, 16), (2, 8, 1, 5)])
 def test_eplb_planner_matches_oracle(seed, E, slices, budget):
     rng = np.random.default_rng(seed)

@@ -227,6 +227,47 @@ def test_route_selection_edge_cases(E, k, dtype, mode, biased):
     assert np.array_equal(host(counts), oracle.expert_counts(rids, E)), "expert counts"
 
 
+# ---------------------------------------------------------- weight image ---
+
+def _packed_image(w: np.ndarray, gateup: bool, H: int, I: int) -> np.ndarray:
+    """The tile image that moe_pack_expert_weights documents, by numpy indexing:
+    block (e, n, s), tile row r, slot j = bytes 64 s + 16 (j ^ ((r >> 2) & 3)) .. +16
+    of weight row row(n, r) (clamped rows in partial n-tiles)."""
+    r = np.arange(256)
+    if gateup:
+        K, NT = H, (I + 127) // 128
+        pair = np.minimum(np.arange(NT)[:, None] * 128 + (r % 128)[None, :], I - 1)
+        rows = np.where(r[None, :] < 128, pair, I + pair)
+    else:
+        K, NT = I, (H + 255) // 256
+        rows = np.minimum(np.arange(NT)[:, None] * 256 + r[None, :], H - 1)
+    chunk = np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3)                  # [256][4]
+    blocks = []
+    for s in range(K // 64):
+        cols = 64 * s + 16 * chunk[:, :, None] + np.arange(16)[None, None, :]  # [256][4][16]
+        blocks.append(w[:, rows[:, :, None, None], cols[None]])               # [E][NT][256][4][16]
+    return np.stack(blocks, axis=2).reshape(-1)
+
+
+def test_pack_expert_weights_image():
+    """The packed weights are the documented tile image byte for byte, for both
+    projections, with partial n-tiles on both (I = 192 pairs of 128-pair tiles,
+    H = 384 rows of 256-row tiles)."""
+    E, H, I = 3, 384, 192
+    rng = np.random.default_rng(11)
+    wgu = rng.integers(-128, 128, (E, 2 * I, H), dtype=np.int8)
+    wd = rng.integers(-128, 128, (E, H, I), dtype=np.int8)
+    sz = moe.moe_plan_sizes(moe.geom(0, H, E, E, 1, 1, 1, 1, 0), I)
+    for w, proj, nbytes in ((wgu, moe.PROJ_GATEUP, sz.w_gateup_packed_bytes),
+                            (wd, moe.PROJ_DOWN, sz.w_down_packed_bytes)):
+        out = torch.empty(nbytes, dtype=torch.int8, device="cuda")
+        moe.moe_pack_expert_weights(to_dev(w), proj, E, H, I, out)
+        torch.cuda.synchronize()
+        ref = _packed_image(w, proj == moe.PROJ_GATEUP, H, I)
+        assert ref.size == nbytes
+        assert np.array_equal(host(out), ref), f"image of projection {proj}"
+
+
 # --------------------------------------------------------------- dispatch ---
 
 @pytest.mark.parametrize("name", ["tiny", "decode96", "ragged"])
