@@ -20,6 +20,22 @@ from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, PROJ_DOWN,
                moe_route_topk, moe_router_logits)
 
 
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _require(name: str, t, shape, dtypes):
+    """The C ABI sees only pointers: a tensor of the wrong size, type or placement
+    would be read out of bounds on the device, so it is refused here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: a torch.Tensor is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: a contiguous device tensor is required")
+
+
 class PackedExpertWeights:
     """The routed experts' INT8 SwiGLU weights on the device, each projection in
     the expert GEMMs' tile image (moe_pack_expert_weights), the fp32 channel
@@ -35,6 +51,10 @@ class PackedExpertWeights:
         if tuple(w_down.shape) != (E, H, I) or w_gateup.dtype != torch.int8 \
                 or w_down.dtype != torch.int8:
             raise ValueError("w_gateup [E][2I][H] and w_down [E][H][I] int8 expected")
+        _require("w_gateup", w_gateup.contiguous(), (E, 2 * I, H), (torch.int8,))
+        _require("w_down", w_down.contiguous(), (E, H, I), (torch.int8,))
+        _require("s_gateup", s_gateup, (E, 2 * I), (torch.float32,))
+        _require("s_down", s_down, (E, H), (torch.float32,))
         self.E, self.H, self.I = E, H, I
         sz = moe_plan_sizes(geom(0, H, E, E, 1, 1, 1, 1, 0), I)
         dev = w_gateup.device
@@ -116,14 +136,27 @@ class MoeLayer:
                  replica_slots: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                  weights=None, I: int = 0, out_dtype: torch.dtype = torch.bfloat16):
         self.g = g
+        if gating not in ("softmax", "sigmoid"):
+            raise ValueError(f"gating {gating!r}: 'softmax' or 'sigmoid'")
         self.gating = GATING_SOFTMAX if gating == "softmax" else GATING_SIGMOID
+        _require("slot_partition", slot_partition, (g.P,), (torch.int32,))
+        _require("slot_logical", slot_logical, (g.P,), (torch.int32,))
+        if (replica_offsets is None) != (replica_slots is None):
+            raise ValueError("replica_offsets and replica_slots go together")
+        if replica_offsets is not None:
+            _require("replica_offsets", replica_offsets, (g.E + 1,), (torch.int32,))
+            if replica_slots.dim() != 1 or replica_slots.numel() < g.P:
+                raise ValueError("replica_slots: a 1-D tensor of at least P entries")
+            _require("replica_slots", replica_slots, replica_slots.shape, (torch.int32,))
+        if bias is not None:
+            _require("bias", bias, (g.E,), (torch.float32,))
         self.slot_partition = slot_partition
         self.slot_logical = slot_logical
         self.replica_offsets = replica_offsets
         self.replica_slots = replica_slots
         self.bias = bias
-        self.weights = weights  # PackedExpertWeights, or a plain 4-tuple packed here, or None
         self.I = I
+        self.weights = weights  # PackedExpertWeights, or a plain 4-tuple packed here, or None
         self.out_dtype = out_dtype
         self.buf = MoeBuffers(g, I, out_dtype)
         self.event_id = 0
@@ -136,25 +169,33 @@ class MoeLayer:
     def weights(self, w):
         """A PackedExpertWeights, None, or (w_gateup, s_gateup, w_down, s_down) device
         tensors in the plain layout, which are packed here (once)."""
-        self._weights = _packed(w)
+        w = _packed(w)
+        if w is not None and (w.E, w.H, w.I) != (self.g.E, self.g.H, self.I):
+            raise ValueError(f"expert weights for E={w.E}, H={w.H}, I={w.I}; the layer has "
+                             f"E={self.g.E}, H={self.g.H}, I={self.I}")
+        self._weights = w
 
     @staticmethod
     def _dt(t: torch.Tensor) -> int:
-        return DTYPE_BF16 if t.dtype in (torch.bfloat16, torch.int16, torch.uint16) else DTYPE_F32
+        return DTYPE_BF16 if t.dtype in _BF16_BITS else DTYPE_F32
 
     def router(self, x, w_router):
         """Gate logits from the hidden states: x [T][H] bf16, w_router [E][H] bf16 ->
         fp32 logits [T][E] (returned; route() takes them)."""
+        _require("x", x, (self.g.T, self.g.H), _BF16_BITS)
+        _require("w_router", w_router, (self.g.E, self.g.H), _BF16_BITS)
         logits, scratch = self.buf.router_buffers()
         moe_router_logits(x, w_router, self.g, logits, scratch)
         return logits
 
     def route(self, logits):
+        _require("logits", logits, (self.g.T, self.g.E), _BF16_BITS + (torch.float32,))
         b = self.buf
         moe_route_topk(logits, self._dt(logits), self.bias, self.gating, self.replica_offsets,
                        self.replica_slots, self.g, b.topk_ids, b.topk_w, b.phys, b.expert_counts)
 
     def dispatch(self, x):
+        _require("x", x, (self.g.T, self.g.H), _BF16_BITS + (torch.float32,))
         b = self.buf
         self.event_id = (self.event_id + 1) & 0xFFFFFFFF
         moe_dispatch_q8(x, self._dt(x), b.phys, self.slot_partition, self.event_id, self.g,

@@ -719,3 +719,42 @@ def test_all_tokens_to_one_partition():
     _, _, phys = _check_route(c)
     q, s, lay = _check_dispatch(c, phys)
     assert lay["meta"][0, :, 2].max() == w.LB * min(w.k, w.Epp)
+
+
+def test_layer_refuses_mismatched_tensors():
+    """The C ABI sees only pointers; the layer refuses tensors whose shape, dtype
+    or placement would make a kernel read out of bounds, before any launch."""
+    w = mw.WORKLOADS["tiny"]
+    g = moe.geom_of(w)
+    ro, rs, sp, sl = mw.identity_map(w)
+    sp_d, sl_d = to_dev(sp), to_dev(sl)
+    with pytest.raises(ValueError):
+        moe.MoeLayer(g, w.gating, sp_d[:-1].contiguous(), sl_d)            # P - 1 slots
+    with pytest.raises(ValueError):
+        moe.MoeLayer(g, w.gating, sp_d, sl_d.to(torch.int64))               # wrong dtype
+    with pytest.raises(ValueError):
+        moe.MoeLayer(g, w.gating, sp_d, sl_d, bias=torch.zeros(w.E + 1, device="cuda"))
+    with pytest.raises(ValueError):
+        moe.MoeLayer(g, "relu", sp_d, sl_d)
+    layer = moe.MoeLayer(g, w.gating, sp_d, sl_d)
+    with pytest.raises(ValueError):
+        layer.route(torch.zeros((w.T, w.E - 1), device="cuda"))             # [T][E-1] logits
+    with pytest.raises(ValueError):
+        layer.dispatch(torch.zeros((w.T, w.H), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        layer.route(torch.zeros((w.E, w.T), device="cuda").t())             # not contiguous
+    # expert weights: scales of the wrong shape, and weights for another I
+    E, H, I = 2, 128, 64
+    wgu = torch.zeros((E, 2 * I, H), dtype=torch.int8, device="cuda")
+    wd = torch.zeros((E, H, I), dtype=torch.int8, device="cuda")
+    sgu, sd = torch.ones((E, 2 * I), device="cuda"), torch.ones((E, H), device="cuda")
+    with pytest.raises(ValueError):
+        moe.PackedExpertWeights(wgu, sgu[:, :I].contiguous(), wd, sd)
+    packed = moe.PackedExpertWeights(wgu, sgu, wd, sd)
+    g2 = moe.geom(T=8, H=H, E=E, P=E, k=1, D=1, Epp=E, S=1, LB=8)
+    eye = torch.arange(E, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        moe.MoeLayer(g2, "sigmoid", torch.zeros(E, dtype=torch.int32, device="cuda"), eye,
+                     weights=packed, I=2 * I)
+    moe.MoeLayer(g2, "sigmoid", torch.zeros(E, dtype=torch.int32, device="cuda"), eye,
+                 weights=packed, I=I)
