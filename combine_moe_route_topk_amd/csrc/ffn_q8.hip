@@ -383,20 +383,21 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       }
     }
     __syncthreads();
-    // max |h| of each row over this n-tile: one thread per row scans the staged
-    // row (a cross-lane reduction per value costs far more)
-    if (tid < BM) {
-      const int64_t rr = row0 + tid;
-      if (tid < rows_here && rr < nrows) {
-        const float4 *rowp = (const float4 *)(stg + tid * kStageStride);
-        float m = 0.0f;
+    // max |h| of each row over this n-tile: two threads per row scan the staged
+    // row, alternate float4 columns each (a cross-lane reduction per value costs
+    // far more); 16 lanes then read 8 rows x 2 columns, on 16 distinct bank groups
+    {
+      const int row = tid >> 1, part = tid & 1;
+      const float4 *rowp = (const float4 *)(stg + row * kStageStride);
+      float m = 0.0f;
 #pragma unroll 8
-        for (int c = 0; c < BN / 2 / 4; ++c) {
-          const float4 v = rowp[c];
-          m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-        pmax[rr * NT + tl.n] = m;
+      for (int c = part; c < BN / 2 / 4; c += 2) {
+        const float4 v = rowp[c];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
       }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      const int64_t rr = row0 + row;
+      if (part == 0 && row < rows_here && rr < nrows) pmax[rr * NT + tl.n] = m;
     }
     // 128 rows x 128 fp32 = 4096 chunks of 4 values
     const int n0 = tl.n * (BN / 2);
@@ -446,22 +447,26 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       // below that the residual can underflow, and the division is used.
       __shared__ float qscale[BM], qrcp[BM];
       uint8_t *retq = (uint8_t *)ret;
-      if (tid < BM) {
-        const uint4 *rowp = (const uint4 *)((const uint8_t *)stb + tid * kStageStrideB);
+      {  // two threads per row, alternate 16-byte chunks (as the gate/up row scan)
+        const int row = tid >> 1, part = tid & 1;
+        const uint4 *rowp = (const uint4 *)((const uint8_t *)stb + row * kStageStrideB);
         float m = 0.0f;
 #pragma unroll 8
-        for (int c = 0; c < BN / 8; ++c) {
+        for (int c = part; c < BN / 8; c += 2) {
           const uint4 v = rowp[c];
           const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wd[q] & 0xffffu)), fabsf(bf16_bits_to_f32(wd[q] >> 16))));
         }
-        const float sq = m / 127.0f;
-        qscale[tid] = sq;
-        qrcp[tid] = sq >= 0x1p-100f ? 1.0f / sq : 0.0f;  // 0: divide
-        const int64_t rr = row0 + tid;
-        if (tid < rows_here && rr < nrows) *(float *)(retq + rr * ret_row_bytes + H + 4 * tl.n) = sq;
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        if (part == 0) {
+          const float sq = m / 127.0f;
+          qscale[row] = sq;
+          qrcp[row] = sq >= 0x1p-100f ? 1.0f / sq : 0.0f;  // 0: divide
+          const int64_t rr = row0 + row;
+          if (row < rows_here && rr < nrows) *(float *)(retq + rr * ret_row_bytes + H + 4 * tl.n) = sq;
+        }
       }
       __syncthreads();
       // 128 rows x 256 columns = 2048 chunks of 16 codes -> one 16-byte store each
