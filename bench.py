@@ -162,28 +162,38 @@ def time_pipeline(layer, x, lg, w, steps, warmup, n_micro=2):
 
 
 def time_router(layer, x, w, steps, warmup):
-    """moe_router_logits on the layer's hidden states: x [T][H] . W_router^T -> fp32 [T][E]."""
+    """The gate from the hidden states, timed alone (the headline step starts from the
+    logits): moe_router_logits (x [T][H] . W_router^T -> fp32 [T][E]), and
+    moe_router_topk (the same logits consumed by the top-k in one call, routes and
+    counts out, logits not kept) next to moe_router_logits + moe_route_topk."""
     import numpy as np
     import torch
     import moe_workloads as mw
     wr = torch.from_numpy(mw.router_weights(w).view(np.int16)).view(torch.bfloat16).cuda()
-    for _ in range(warmup):
-        layer.router(x, wr)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        layer.router(x, wr)
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    us = timed(lambda: layer.router(x, wr))
+    two = timed(lambda: layer.route(layer.router(x, wr)))
+    fused = timed(lambda: layer.route_from_hidden(x, wr))
     flops = 2.0 * w.T * w.E * w.H
     nbytes = w.T * w.H * 2 + w.E * w.H * 2 + w.T * w.E * 4
     return {"us": round(us, 2), "TFLOPS": round(flops / (us * 1e-6) / 1e12, 1),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "splits": int(layer.buf.sizes.router_scratch_bytes // (w.T * w.E * 4)),
+            "gate_and_topk_us": {"two_calls": round(two, 2), "fused": round(fused, 2)},
             "note": "bf16 MFMA, fp32 accumulation; timed alone (the workload's step starts "
-                    "from the logits)"}
+                    "from the logits); fused = moe_router_topk"}
 
 
 def attainable(w, reps=5):

@@ -34,7 +34,7 @@ PROJ_GATEUP, PROJ_DOWN = 0, 1
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
-            "moe_pack_expert_weights", "moe_status_string")
+            "moe_pack_expert_weights", "moe_router_topk", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -92,6 +92,8 @@ def lib():
         L.moe_expert_down_q8_int8ret.argtypes = L.moe_expert_down_q8.argtypes
         L.moe_router_logits.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P, ctypes.c_size_t, _P]
         L.moe_pack_expert_weights.argtypes = [_P, _I32, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]
+        L.moe_router_topk.argtypes = [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(Geom), _P, _P, _P,
+                                      _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -225,6 +227,16 @@ def moe_router_logits(x, w_router, g: Geom, logits, scratch, stream=None):
     _check(lib().moe_router_logits(_ptr(x), _ptr(w_router), ctypes.byref(g), _ptr(logits),
                                    _ptr(scratch), scratch.numel() * scratch.element_size(),
                                    _stream(stream)), "moe_router_logits")
+
+
+def moe_router_topk(x, w_router, bias, gating: int, replica_offsets, replica_slots, g: Geom,
+                    logits, topk_ids, topk_w, phys_ids, expert_counts, scratch, stream=None):
+    _check(lib().moe_router_topk(_ptr(x), _ptr(w_router), _ptr(bias), gating,
+                                 _ptr(replica_offsets), _ptr(replica_slots), ctypes.byref(g),
+                                 _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(phys_ids),
+                                 _ptr(expert_counts), _ptr(scratch),
+                                 scratch.numel() * scratch.element_size(), _stream(stream)),
+           "moe_router_topk")
 
 
 def moe_pack_expert_weights(w, proj: int, E: int, H: int, I: int, packed, stream=None):

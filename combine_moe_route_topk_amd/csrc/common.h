@@ -58,6 +58,12 @@ inline int64_t chunks_per_source(const moe_geom_t &g) {
 }
 
 int validate_geom(const moe_geom_t *g);
+// Gate logits as router_splits(g) partial sums [splits][T][E] (ffn_q8.hip), and
+// the host checks shared by the two gate entry points.
+int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *part,
+                    hipStream_t s);
+int router_check(const void *x, const void *w_router, const moe_geom_t *g, void *scratch,
+                 size_t scratch_bytes);
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }

@@ -768,33 +768,51 @@ extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count
                             acc_down_dbg, scratch, scratch_bytes, stream);
 }
 
-extern "C" int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g,
-                                 float *logits, void *scratch, size_t scratch_bytes,
-                                 void *stream) {
-  int st = validate_geom(g);
-  if (st != MOE_OK) return st;
-  const int ks = router_splits(*g);
-  if (ks == 0 || g->E % 4 != 0) return MOE_ERR_UNSUPPORTED;
-  if (g->T == 0) return MOE_OK;
-  if (!x || !w_router || !logits || !scratch) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) || !aligned16(scratch))
-    return MOE_ERR_INVALID_ARG;
-  if ((int64_t)scratch_bytes < router_scratch_bytes_of(*g)) return MOE_ERR_CAPACITY;
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t mt = ((int64_t)g->T + BM - 1) / BM, nt = (g->E + BN - 1) / BN;
+namespace moe {
+
+// Partial gate logits of the router_splits(g) K splits into part [splits][T][E]
+// (fp32); the caller has validated the geometry, pointers and scratch size.
+int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *part,
+                    hipStream_t s) {
+  const int ks = router_splits(g);
+  const int64_t mt = ((int64_t)g.T + BM - 1) / BM, nt = (g.E + BN - 1) / BN;
   const int64_t blocks = (mt * nt * ks + kXcds - 1) / kXcds * kXcds;
-  float *part = (float *)scratch;
   hipLaunchKernelGGL((ffn_gemm_kernel<ROUTER, false>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const int32_t *)nullptr, (const int32_t *)nullptr, (const int32_t *)nullptr,
                      (const int32_t *)nullptr, (const int32_t *)nullptr, (const uint8_t *)x,
                      (int64_t)0, (const int8_t *)nullptr, (const float *)nullptr,
-                     (const int8_t *)w_router, (const float *)nullptr, ks, g->E, g->H, 0,
-                     (int64_t)g->T, part, (float *)nullptr, (uint16_t *)nullptr, (int64_t)0,
+                     (const int8_t *)w_router, (const float *)nullptr, ks, g.E, g.H, 0,
+                     (int64_t)g.T, part, (float *)nullptr, (uint16_t *)nullptr, (int64_t)0,
                      (int32_t *)nullptr);
-  if ((st = launch_status()) != MOE_OK) return st;
+  return launch_status();
+}
+
+int router_check(const void *x, const void *w_router, const moe_geom_t *g, void *scratch,
+                 size_t scratch_bytes) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (router_splits(*g) == 0 || g->E % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (g->T == 0) return MOE_OK;
+  if (!x || !w_router || !scratch) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(scratch)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)scratch_bytes < router_scratch_bytes_of(*g)) return MOE_ERR_CAPACITY;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g,
+                                 float *logits, void *scratch, size_t scratch_bytes,
+                                 void *stream) {
+  int st = router_check(x, w_router, g, scratch, scratch_bytes);
+  if (st != MOE_OK || g->T == 0) return st;
+  if (!logits || !aligned16(logits)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  float *part = (float *)scratch;
+  if ((st = router_partials(x, w_router, *g, part, s)) != MOE_OK) return st;
   const int64_t n = (int64_t)g->T * g->E;
   hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                     part, n, ks, logits);
+                     part, n, router_splits(*g), logits);
   return launch_status();
 }
 

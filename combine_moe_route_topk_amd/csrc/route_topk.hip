@@ -39,9 +39,12 @@ __global__ void zero_i32(int32_t *p, int n) {
 
 // Loads the EPL raw logits of one lane (FULL: E == 64*EPL, so the lane's
 // run is whole and aligned to its size and can go as one vector load).
+// fp32 logits may come as nsplit partial sums split_stride floats apart (the
+// gate GEMM's K splits), added in split order: the same fp32 sums as the
+// gate's own reduction, so the logits are the same bits.
 template <int EPL, bool BF16, bool FULL>
 __device__ __forceinline__ void load_row(const void *logits, int64_t t, int E, int lane,
-                                         float (&v)[EPL]) {
+                                         int nsplit, int64_t split_stride, float (&v)[EPL]) {
   if constexpr (BF16) {
     const uint16_t *row = (const uint16_t *)logits + t * E + lane * EPL;
     if constexpr (FULL) {
@@ -56,15 +59,20 @@ __device__ __forceinline__ void load_row(const void *logits, int64_t t, int E, i
     }
   } else {
     const float *row = (const float *)logits + t * E + lane * EPL;
-    if constexpr (FULL) {
-      constexpr int kAlign = EPL * 4 >= 16 ? 16 : EPL * 4;
-      const float *p = (const float *)__builtin_assume_aligned(row, kAlign);
+    for (int sp = 0; sp < nsplit; ++sp, row += split_stride) {
+      float u[EPL];
+      if constexpr (FULL) {
+        constexpr int kAlign = EPL * 4 >= 16 ? 16 : EPL * 4;
+        const float *p = (const float *)__builtin_assume_aligned(row, kAlign);
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) v[i] = __builtin_nontemporal_load(p + i);
-    } else {
+        for (int i = 0; i < EPL; ++i) u[i] = __builtin_nontemporal_load(p + i);
+      } else {
 #pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        v[i] = lane * EPL + i < E ? __builtin_nontemporal_load(row + i) : 0.0f;
+        for (int i = 0; i < EPL; ++i)
+          u[i] = lane * EPL + i < E ? __builtin_nontemporal_load(row + i) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i] = sp == 0 ? u[i] : v[i] + u[i];
     }
   }
 }
@@ -73,8 +81,9 @@ template <int EPL, bool BF16, bool FULL>
 __global__ __launch_bounds__(kBlock) void route_topk_kernel(
     const void *__restrict__ logits, const float *__restrict__ bias, int gating,
     const int32_t *__restrict__ roff, const int32_t *__restrict__ rslots, int T, int E, int P,
-    int k, int LB, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
-    int32_t *__restrict__ phys_ids, int32_t *__restrict__ expert_counts) {
+    int k, int LB, int nsplit, int64_t split_stride, float *__restrict__ logits_out,
+    int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ phys_ids,
+    int32_t *__restrict__ expert_counts) {
   extern __shared__ int32_t hist[];  // [E] when expert_counts != nullptr
   const int lane = threadIdx.x & 63;
   if (expert_counts) {
@@ -93,12 +102,17 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   float raw[EPL];
-  if (t < T) load_row<EPL, BF16, FULL>(logits, t, E, lane, raw);
+  if (t < T) load_row<EPL, BF16, FULL>(logits, t, E, lane, nsplit, split_stride, raw);
   for (; t < T; t += nwaves) {
+    if (logits_out) {  // the summed logits, for callers that keep them
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane * EPL + i < E) logits_out[t * E + lane * EPL + i] = raw[i];
+    }
     uint32_t ord[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) ord[i] = lane * EPL + i < E ? order_key(raw[i] + bv[i]) : 0u;
-    if (t + nwaves < T) load_row<EPL, BF16, FULL>(logits, t + nwaves, E, lane, raw);
+    if (t + nwaves < T) load_row<EPL, BF16, FULL>(logits, t + nwaves, E, lane, nsplit, split_stride, raw);
 
     // radix select of the k-th largest key (invalid lanes hold 0, below every
     // candidate, and lose every tie on id)
@@ -212,8 +226,15 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
   }
 }
 
+struct RouteIn {  // the logits: one array, or nsplit partial sums split_stride apart
+  const void *logits;
+  int nsplit;
+  int64_t split_stride;
+  float *logits_out;  // the summed logits are written here when not null
+};
+
 template <int EPL, bool BF16, bool FULL>
-hipError_t launch_route3(const void *logits, const float *bias, int gating, const int32_t *roff,
+hipError_t launch_route3(const RouteIn &in, const float *bias, int gating, const int32_t *roff,
                          const int32_t *rslots, const moe_geom_t &g, int32_t *ids, float *w,
                          int32_t *phys, int32_t *counts, hipStream_t st) {
   const int waves = kBlock / 64;
@@ -221,25 +242,65 @@ hipError_t launch_route3(const void *logits, const float *bias, int gating, cons
   const size_t lds = counts ? sizeof(int32_t) * g.E : 0;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((route_topk_kernel<EPL, BF16, FULL>), dim3(blocks), dim3(kBlock), lds, st,
-                     logits, bias, gating, roff, rslots, g.T, g.E, g.P, g.k, g.LB, ids, w, phys,
-                     counts);
+                     in.logits, bias, gating, roff, rslots, g.T, g.E, g.P, g.k, g.LB, in.nsplit,
+                     in.split_stride, in.logits_out, ids, w, phys, counts);
   return hipGetLastError();
 }
 
 template <int EPL>
-hipError_t launch_route(const void *logits, bool bf16, const float *bias, int gating,
+hipError_t launch_route(const RouteIn &in, bool bf16, const float *bias, int gating,
                         const int32_t *roff, const int32_t *rslots, const moe_geom_t &g,
                         int32_t *ids, float *w, int32_t *phys, int32_t *counts, hipStream_t st) {
   const bool full = g.E == 64 * EPL;
   if (bf16)
-    return full ? launch_route3<EPL, true, true>(logits, bias, gating, roff, rslots, g, ids, w,
-                                                 phys, counts, st)
-                : launch_route3<EPL, true, false>(logits, bias, gating, roff, rslots, g, ids, w,
-                                                  phys, counts, st);
-  return full ? launch_route3<EPL, false, true>(logits, bias, gating, roff, rslots, g, ids, w, phys,
+    return full ? launch_route3<EPL, true, true>(in, bias, gating, roff, rslots, g, ids, w, phys,
+                                                 counts, st)
+                : launch_route3<EPL, true, false>(in, bias, gating, roff, rslots, g, ids, w, phys,
+                                                  counts, st);
+  return full ? launch_route3<EPL, false, true>(in, bias, gating, roff, rslots, g, ids, w, phys,
                                                 counts, st)
-              : launch_route3<EPL, false, false>(logits, bias, gating, roff, rslots, g, ids, w,
-                                                 phys, counts, st);
+              : launch_route3<EPL, false, false>(in, bias, gating, roff, rslots, g, ids, w, phys,
+                                                 counts, st);
+}
+
+// Checks shared by the two top-k entry points (no launch on error).
+int route_check(moe_gating_t gating, const int32_t *roff, const int32_t *rslots,
+                const moe_geom_t *g, int32_t *topk_ids, float *topk_w, int32_t *phys_ids) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (g->T > 0 && (!topk_ids || !topk_w || !phys_ids)) return MOE_ERR_INVALID_ARG;
+  if (gating != MOE_GATING_SOFTMAX && gating != MOE_GATING_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if ((roff == nullptr) != (rslots == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!roff && g->P != g->E) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int route_run(const RouteIn &in, bool bf16, const float *bias, moe_gating_t gating,
+              const int32_t *roff, const int32_t *rslots, const moe_geom_t *g, int32_t *topk_ids,
+              float *topk_w, int32_t *phys_ids, int32_t *expert_counts, hipStream_t s) {
+  int st;
+  if (expert_counts) {
+    hipLaunchKernelGGL(zero_i32, dim3((g->E + 255) / 256), dim3(256), 0, s, expert_counts, g->E);
+    if ((st = launch_status()) != MOE_OK) return st;
+  }
+  hipError_t e;
+  const int E = g->E;
+  if (E <= 64)
+    e = launch_route<1>(in, bf16, bias, gating, roff, rslots, *g, topk_ids, topk_w, phys_ids,
+                        expert_counts, s);
+  else if (E <= 128)
+    e = launch_route<2>(in, bf16, bias, gating, roff, rslots, *g, topk_ids, topk_w, phys_ids,
+                        expert_counts, s);
+  else if (E <= 256)
+    e = launch_route<4>(in, bf16, bias, gating, roff, rslots, *g, topk_ids, topk_w, phys_ids,
+                        expert_counts, s);
+  else if (E <= 512)
+    e = launch_route<8>(in, bf16, bias, gating, roff, rslots, *g, topk_ids, topk_w, phys_ids,
+                        expert_counts, s);
+  else
+    e = launch_route<16>(in, bf16, bias, gating, roff, rslots, *g, topk_ids, topk_w, phys_ids,
+                         expert_counts, s);
+  return hip_status(e);
 }
 
 }  // namespace
@@ -252,35 +313,29 @@ extern "C" int moe_route_topk(const void *logits, moe_dtype_t logits_dtype, cons
                               const int32_t *replica_slots, const moe_geom_t *g, int32_t *topk_ids,
                               float *topk_w, int32_t *phys_ids, int32_t *expert_counts,
                               void *stream) {
-  int st = validate_geom(g);
+  int st = route_check(gating, replica_offsets, replica_slots, g, topk_ids, topk_w, phys_ids);
   if (st != MOE_OK) return st;
-  if (g->T > 0 && (!logits || !topk_ids || !topk_w || !phys_ids)) return MOE_ERR_INVALID_ARG;
+  if (g->T > 0 && !logits) return MOE_ERR_INVALID_ARG;
   if (logits_dtype != MOE_DTYPE_F32 && logits_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
-  if (gating != MOE_GATING_SOFTMAX && gating != MOE_GATING_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if ((replica_offsets == nullptr) != (replica_slots == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (!replica_offsets && g->P != g->E) return MOE_ERR_INVALID_ARG;
+  const RouteIn in{logits, 1, 0, nullptr};
+  return route_run(in, logits_dtype == MOE_DTYPE_BF16, bias, gating, replica_offsets,
+                   replica_slots, g, topk_ids, topk_w, phys_ids, expert_counts,
+                   (hipStream_t)stream);
+}
+
+extern "C" int moe_router_topk(const void *x, const void *w_router, const float *bias,
+                               moe_gating_t gating, const int32_t *replica_offsets,
+                               const int32_t *replica_slots, const moe_geom_t *g, float *logits,
+                               int32_t *topk_ids, float *topk_w, int32_t *phys_ids,
+                               int32_t *expert_counts, void *scratch, size_t scratch_bytes,
+                               void *stream) {
+  int st = route_check(gating, replica_offsets, replica_slots, g, topk_ids, topk_w, phys_ids);
+  if (st != MOE_OK) return st;
+  if ((st = router_check(x, w_router, g, scratch, scratch_bytes)) != MOE_OK || g->T == 0) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (expert_counts) {
-    hipLaunchKernelGGL(zero_i32, dim3((g->E + 255) / 256), dim3(256), 0, s, expert_counts, g->E);
-    if ((st = launch_status()) != MOE_OK) return st;
-  }
-  const bool bf16 = logits_dtype == MOE_DTYPE_BF16;
-  hipError_t e;
-  const int E = g->E;
-  if (E <= 64)
-    e = launch_route<1>(logits, bf16, bias, gating, replica_offsets, replica_slots, *g, topk_ids,
-                        topk_w, phys_ids, expert_counts, s);
-  else if (E <= 128)
-    e = launch_route<2>(logits, bf16, bias, gating, replica_offsets, replica_slots, *g, topk_ids,
-                        topk_w, phys_ids, expert_counts, s);
-  else if (E <= 256)
-    e = launch_route<4>(logits, bf16, bias, gating, replica_offsets, replica_slots, *g, topk_ids,
-                        topk_w, phys_ids, expert_counts, s);
-  else if (E <= 512)
-    e = launch_route<8>(logits, bf16, bias, gating, replica_offsets, replica_slots, *g, topk_ids,
-                        topk_w, phys_ids, expert_counts, s);
-  else
-    e = launch_route<16>(logits, bf16, bias, gating, replica_offsets, replica_slots, *g, topk_ids,
-                         topk_w, phys_ids, expert_counts, s);
-  return hip_status(e);
+  float *part = (float *)scratch;
+  if ((st = router_partials(x, w_router, *g, part, s)) != MOE_OK) return st;
+  const RouteIn in{part, router_splits(*g), (int64_t)g->T * g->E, logits};
+  return route_run(in, false, bias, gating, replica_offsets, replica_slots, g, topk_ids, topk_w,
+                   phys_ids, expert_counts, s);
 }

@@ -17,7 +17,7 @@ from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, PROJ_DOWN,
                RET_BF16, RET_Q8_BLOCKS, RET_Q8_FROM_DISPATCH, Geom, geom, moe_combine,
                moe_dispatch_q8, moe_expert_down_q8, moe_expert_down_q8_int8ret, moe_expert_ffn_q8,
                moe_expert_gateup_q8, moe_pack_expert_weights, moe_plan_sizes, moe_relay_returns,
-               moe_route_topk, moe_router_logits)
+               moe_route_topk, moe_router_logits, moe_router_topk)
 
 
 _BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
@@ -187,6 +187,18 @@ class MoeLayer:
         logits, scratch = self.buf.router_buffers()
         moe_router_logits(x, w_router, self.g, logits, scratch)
         return logits
+
+    def route_from_hidden(self, x, w_router, keep_logits: bool = False):
+        """The gate and the routing in one call (moe_router_topk): fills the same
+        route buffers as route(); returns the fp32 logits when keep_logits."""
+        _require("x", x, (self.g.T, self.g.H), _BF16_BITS)
+        _require("w_router", w_router, (self.g.E, self.g.H), _BF16_BITS)
+        logits, scratch = self.buf.router_buffers()
+        b = self.buf
+        moe_router_topk(x, w_router, self.bias, self.gating, self.replica_offsets,
+                        self.replica_slots, self.g, logits if keep_logits else None, b.topk_ids,
+                        b.topk_w, b.phys, b.expert_counts, scratch)
+        return logits if keep_logits else None
 
     def route(self, logits):
         _require("logits", logits, (self.g.T, self.g.E), _BF16_BITS + (torch.float32,))

@@ -126,7 +126,7 @@ typedef struct moe_sizes {
   int64_t ffn_scratch_bytes;           /* scratch of moe_expert_ffn_q8 (I > 0)            */
   int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256), 16B   */
   int64_t ret_q8_bytes;                /* T * k INT8 return rows                          */
-  int64_t router_scratch_bytes;        /* scratch of moe_router_logits                    */
+  int64_t router_scratch_bytes;        /* scratch of moe_router_logits / moe_router_topk  */
   int64_t w_gateup_packed_bytes;       /* moe_pack_expert_weights image, MOE_PROJ_GATEUP  */
   int64_t w_down_packed_bytes;         /* moe_pack_expert_weights image, MOE_PROJ_DOWN    */
 } moe_sizes_t;
@@ -203,6 +203,26 @@ int moe_route_topk(const void *logits, moe_dtype_t logits_dtype, const float *bi
  */
 int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g, float *logits,
                       void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * moe_router_topk -- the gate from the hidden states to the routes in one call
+ * [CMI EP320 fused_moe listing: gate.topk(hidden, k = 8); XDS 专家负载均衡 P068
+ * (the collect step) and P078-P079 (the replica gather)]: the logits of
+ * moe_router_logits, then moe_route_topk on them (MOE_DTYPE_F32), without the
+ * logits' round trip through memory: the top-k reads the gate's K-split partial
+ * sums and adds them in split order itself, so logits, ids, weights, physical
+ * ids and counts are the same bits as the two calls give.
+ *   x, w_router, scratch  as moe_router_logits (router_scratch_bytes)
+ *   logits   [T][E] fp32, or NULL when the caller does not keep them
+ *   bias, gating, replica_offsets, replica_slots, topk_ids, topk_w, phys_ids,
+ *   expert_counts  as moe_route_topk
+ * Errors: those of the two calls.
+ */
+int moe_router_topk(const void *x, const void *w_router, const float *bias, moe_gating_t gating,
+                    const int32_t *replica_offsets, const int32_t *replica_slots,
+                    const moe_geom_t *g, float *logits, int32_t *topk_ids, float *topk_w,
+                    int32_t *phys_ids, int32_t *expert_counts, void *scratch,
+                    size_t scratch_bytes, void *stream);
 
 /*
  * moe_dispatch_q8 -- token-wise INT8 quantization fused into the scatter into

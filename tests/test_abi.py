@@ -153,6 +153,24 @@ def test_pack_expert_weights_validation_and_sizes():
                                      None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_router_topk_validation():
+    """The one-call gate + top-k checks both halves' arguments on the host and
+    returns before any launch (runs without a GPU)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    g = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    s = moe.moe_plan_sizes(g, 0)
+    args = lambda **kw: [kw.get("x", fake), fake, None, kw.get("gating", moe.GATING_SIGMOID),
+                         kw.get("ro", None), None, ctypes.byref(kw.get("g", g)), None, fake, fake,
+                         fake, None, fake, kw.get("sb", s.router_scratch_bytes), None]
+    assert L.moe_router_topk(*args(gating=5)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_topk(*args(ro=fake)) == moe.MOE_ERR_INVALID_ARG     # offsets without slots
+    assert L.moe_router_topk(*args(sb=s.router_scratch_bytes - 1)) == moe.MOE_ERR_CAPACITY
+    assert L.moe_router_topk(*args(x=ctypes.c_void_p(0x1008))) == moe.MOE_ERR_INVALID_ARG
+    odd_e = moe.geom(T=16, H=256, E=6, P=6, k=2, D=3, Epp=2, S=4, LB=4)
+    assert L.moe_router_topk(*args(g=odd_e)) == moe.MOE_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("seed,E,slices,budget", [(0, 32, 4, 8), (1, 64, 3, 16), (2, 8, 1, 5)])
 def test_eplb_planner_matches_oracle(seed, E, slices, budget):
     rng = np.random.default_rng(seed)

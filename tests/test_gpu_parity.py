@@ -165,6 +165,33 @@ def test_router_logits_and_topk(name):
     assert_close(host(b.topk_w), tw, FP32_RTOL, FP32_ATOL, "top-k weights")
 
 
+@pytest.mark.parametrize("name", ["ragged", "decode96", "eplb4096"])
+def test_router_topk_fused_equals_two_calls(name):
+    """moe_router_topk (the top-k reading the gate's K-split partial sums) gives
+    the same bits as moe_router_logits followed by moe_route_topk on fp32 logits:
+    logits, ids, weights, physical ids (eplb4096: through the replica map) and
+    expert counts; and the same routes when the logits are not kept."""
+    w = RAGGED if name == "ragged" else mw.WORKLOADS[name]
+    c = Case(w)
+    wr = dev_bits(mw.router_weights(w), True)
+    logits = c.layer.router(c.x_d, wr).clone()
+    c.layer.route(logits)
+    b = c.layer.buf
+    outs = (b.topk_ids, b.topk_w, b.phys, b.expert_counts)
+    ref = [host(t).copy() for t in outs]
+    for keep in (True, False):
+        for t in outs:
+            t.fill_(-7)
+        got = c.layer.route_from_hidden(c.x_d, wr, keep_logits=keep)
+        torch.cuda.synchronize()
+        if keep:
+            assert np.array_equal(host(got).view(np.uint32), host(logits).view(np.uint32)), "logits"
+        for label, t, r in zip(("ids", "weights", "physical ids", "counts"), outs, ref):
+            a = host(t)
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  r.view(np.uint32) if r.dtype == np.float32 else r), label
+
+
 def test_router_logits_layer12288_sampled_tokens():
     """The gate at the headline shape (T = 12288, H = 7168, E = 256): 96 sampled
     tokens' logits within the fp32 bound of the exact values."""
