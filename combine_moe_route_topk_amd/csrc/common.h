@@ -33,16 +33,18 @@ inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
   return ((int64_t)g.H + 4 * nblk + 15) / 16 * 16;
 }
 
-// Tile image of the INT8 expert weights (moe_pack_expert_weights): one 16 KB
-// block per (expert, n-tile, 64-byte K step), n-tiles of 128 gate/up pairs
-// (gate/up) or 256 output channels (down).
+// Image of the INT8 expert weights (moe_pack_expert_weights): one 16 KB block
+// per (expert, n-tile, 64-byte K step), n-tiles of 128 gate/up pairs
+// (gate/up) or 256 output channels (down), K padded to whole groups of four
+// steps.
 constexpr int64_t kPackedStepBytes = 256 * 64;
 __host__ __device__ inline int packed_ntiles(int proj, int H, int I) {
   return proj == MOE_PROJ_GATEUP ? (I + 127) / 128 : (H + 255) / 256;
 }
+__host__ __device__ inline int packed_ksteps(int K) { return (K / 64 + 3) & ~3; }
 inline int64_t packed_weight_bytes(int proj, int E, int H, int I) {
   const int K = proj == MOE_PROJ_GATEUP ? H : I;
-  return (int64_t)E * packed_ntiles(proj, H, I) * (K / 64) * kPackedStepBytes;
+  return (int64_t)E * packed_ntiles(proj, H, I) * packed_ksteps(K) * kPackedStepBytes;
 }
 
 // Routes per dispatch chunk: chunks never straddle a source partition.

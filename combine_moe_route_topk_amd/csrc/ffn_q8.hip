@@ -20,9 +20,10 @@
 // Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
 // each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes moved global -> LDS by
 // DMA into a ring of three stages, two steps ahead, XOR-swizzled rows.  The
-// weights come pre-packed in the LDS image of each (n-tile, K step) (see
-// moe_pack_expert_weights), so a step's 16 KB of B is one contiguous run of
-// whole cache lines rather than 256 half lines.  The
+// weights come pre-packed (moe_pack_expert_weights) in MFMA fragment order:
+// each wavefront loads its own 64 columns of a K step straight into
+// registers, 4 KB as four contiguous 1 KB runs of whole cache lines, three
+// steps ahead of the MFMAs; A alone goes through the LDS ring.  The
 // work list is ordered slot-major, then groups of kGroupM m-tiles, then
 // n-tiles, then m inside the group, and blocks are remapped so that each XCD
 // walks one contiguous stretch of it: the m-tiles of a group share every
@@ -234,30 +235,12 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     return (const uint8_t *)w + (int64_t)min(tl.n * BN + r, E - 1) * 2 * H + (int64_t)ksplit * K + c;
   };
   const uint8_t *pa0 = a_row_ptr(16 * (2 * wv) + lrow), *pa1 = a_row_ptr(16 * (2 * wv + 1) + lrow);
-  // B sources: W_router rows (ROUTER), else this wave's four 1 KB chunks of
-  // the packed weight block of (e, n-tile, K step), lane i at byte 16 i
-  const uint8_t *pb[4];
-  int64_t b_step;
-  if constexpr (MODE == ROUTER) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pb[c] = b_row_ptr(16 * (4 * wv + c) + lrow);
-    b_step = BK;
-  } else {
-    const uint8_t *blk = (const uint8_t *)w + ((int64_t)e * NT + tl.n) * (K / BK) * kPackedStepBytes;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pb[c] = blk + (4 * wv + c) * 1024 + lane * 16;
-    b_step = kPackedStepBytes;
-  }
-  auto dma = [&](int kstep, int buf) {
-    const int64_t off = (int64_t)kstep * BK, boff = (int64_t)kstep * b_step;
-    uint8_t *la = lds_a(buf) + 2 * wv * 1024;
-    uint8_t *lb = lds_b(buf) + 4 * wv * 1024;
+  // A: the DMA of one K step (wave w: A chunks 2w, 2w + 1) into an LDS stage
+  auto dma_a = [&](int kstep, uint8_t *stage) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)kstep * BK;
+    uint8_t *la = stage + 2 * wv * 1024;
     __builtin_amdgcn_global_load_lds(pa0 + off, (MOE_LDS void *)(la), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(pa1 + off, (MOE_LDS void *)(la + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb[0] + boff, (MOE_LDS void *)(lb), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb[1] + boff, (MOE_LDS void *)(lb + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb[2] + boff, (MOE_LDS void *)(lb + 2048), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pb[3] + boff, (MOE_LDS void *)(lb + 3072), 16, 0, 0);
   };
 
   // B-tile rows of this wave's two 32-column blocks
@@ -279,52 +262,167 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // start at multiples of 32, so the swizzle depends on the lane only)
   const int koff0 = ((0 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
   const int koff1 = ((2 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
-  // Per K step: every wave waits until its own DMA of this step has landed
-  // (the DMA of the next step may still be in flight) and meets the others at
-  // the barrier, so the step's LDS stage is complete and the stage read one
-  // step ago is free; it reads all of the step's fragments, starts the DMA
-  // two steps ahead into that free stage, then runs the 16 MFMAs.
-  dma(0, 0);
-  if (KT > 1) dma(1, 1);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt % kStages;
-    if (kt + 1 < KT)
-      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): all but the next step's 6 DMAs
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    // fragment reads as raw ds_read_b128: the compiler's wait-count pass would
-    // otherwise order them after every DMA in flight (vmcnt(0)), undoing the
-    // ring; the explicit lgkmcnt(0) below makes the results safe to use.
-    const uint32_t la = lds_addr(lds_a(cur)) + (lane & 31) * LDS_STRIDE;
-    const uint32_t lb = lds_addr(lds_b(cur)) + (lane & 31) * LDS_STRIDE;
-    v4i bf[2][2], af[2][MB];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t koff = ks ? koff1 : koff0;
-      bf[ks][0] = ds_read16(lb + nbo0 * LDS_STRIDE + koff);
-      bf[ks][1] = ds_read16(lb + nbo1 * LDS_STRIDE + koff);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) af[ks][mb] = ds_read16(la + mb * 32 * LDS_STRIDE + koff);
-    }
-    if (kt + 2 < KT) dma(kt + 2, (kt + 2) % kStages);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragments are in registers
-    __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMAs
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (mb >= mb_live) break;  // 32-row blocks past the slot's rows: nothing to compute
-        if constexpr (MODE == ROUTER) {
-          const v8bf a = __builtin_bit_cast(v8bf, af[ks][mb]);
-          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][0]), acc[mb][0], 0, 0, 0);
-          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][1]), acc[mb][1], 0, 0, 0);
-        } else {
-          acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
-          acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
+  if constexpr (MODE == ROUTER) {
+    // Per K step: every wave waits until its own DMA of this step has landed
+    // (the DMA of the next step may still be in flight) and meets the others at
+    // the barrier, so the step's LDS stage is complete and the stage read one
+    // step ago is free; it reads all of the step's fragments, starts the DMA
+    // two steps ahead into that free stage, then runs the 16 MFMAs.
+    // B: W_router rows, this wave's B chunks 4w .. 4w + 3 of the step
+    const uint8_t *pb[4];
+  #pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = b_row_ptr(16 * (4 * wv + c) + lrow);
+    auto dma = [&](int kstep, int buf) {
+      const int64_t off = (int64_t)kstep * BK;
+      dma_a(kstep, lds_a(buf));
+      uint8_t *lb = lds_b(buf) + 4 * wv * 1024;
+  #pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_global_load_lds(pb[c] + off, (MOE_LDS void *)(lb + c * 1024), 16, 0, 0);
+    };
+    dma(0, 0);
+    if (KT > 1) dma(1, 1);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt % kStages;
+      if (kt + 1 < KT)
+        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): all but the next step's 6 DMAs
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      // fragment reads as raw ds_read_b128: the compiler's wait-count pass would
+      // otherwise order them after every DMA in flight (vmcnt(0)), undoing the
+      // ring; the explicit lgkmcnt(0) below makes the results safe to use.
+      const uint32_t la = lds_addr(lds_a(cur)) + (lane & 31) * LDS_STRIDE;
+      const uint32_t lb = lds_addr(lds_b(cur)) + (lane & 31) * LDS_STRIDE;
+      v4i bf[2][2], af[2][MB];
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t koff = ks ? koff1 : koff0;
+        bf[ks][0] = ds_read16(lb + nbo0 * LDS_STRIDE + koff);
+        bf[ks][1] = ds_read16(lb + nbo1 * LDS_STRIDE + koff);
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb) af[ks][mb] = ds_read16(la + mb * 32 * LDS_STRIDE + koff);
+      }
+      if (kt + 2 < KT) dma(kt + 2, (kt + 2) % kStages);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragments are in registers
+      __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMAs
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if (mb >= mb_live) break;  // 32-row blocks past the slot's rows: nothing to compute
+          if constexpr (MODE == ROUTER) {
+            const v8bf a = __builtin_bit_cast(v8bf, af[ks][mb]);
+            acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][0]), acc[mb][0], 0, 0, 0);
+            acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][1]), acc[mb][1], 0, 0, 0);
+          } else {
+            acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
+            acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
+          }
         }
       }
     }
+  } else {
+    // B straight from the packed image into registers, three K steps ahead, in a
+    // ring of four register buffers: each wavefront reads only its own 64
+    // columns, 4 KB per step as four 1 KB runs in MFMA fragment order (the image
+    // holds them so); A keeps the LDS DMA, at the same distance, so one vmcnt per
+    // step covers both (vector loads complete in order).  The weight loads are
+    // inline assembly the compiler does not track: its wait-count pass cannot
+    // follow a register ring across the loop edge and would drain every load in
+    // flight at each group of steps.  Their safety is a property of the
+    // generated code -- no instruction may touch a destination register between
+    // its load and the MFMA that reads it, and no load may be in flight when the
+    // loop ends -- which the library's build checks on the assembly.  The steps
+    // are padded to a whole number of groups of four (zero weights in the
+    // image), the loop issues its loads unconditionally, and the last three
+    // steps issue none and wait statically (12, 6, 0 loads in flight).
+    constexpr int kDepth = 3, kAStages = 4;
+    static_assert(kAStages * BM * LDS_STRIDE <= kStages * (BM + BN) * LDS_STRIDE, "A ring fits");
+    const int KTp = (KT + 3) & ~3;
+    const uint8_t *bsrc = (const uint8_t *)w + ((int64_t)e * NT + tl.n) * KTp * kPackedStepBytes +
+                          wv * 4096 + lane * 16;
+    v4i breg[4][2][2];
+    auto load_b = [&](auto bi, int kstep) __attribute__((always_inline)) {
+      constexpr int B = decltype(bi)::value;
+      const uint8_t *p = bsrc + (int64_t)kstep * kPackedStepBytes;
+      v4i t0, t1, t2, t3;
+      asm volatile("global_load_dwordx4 %0, %4, off\n\t"
+                   "global_load_dwordx4 %1, %4, off offset:1024\n\t"
+                   "global_load_dwordx4 %2, %4, off offset:2048\n\t"
+                   "global_load_dwordx4 %3, %4, off offset:3072"
+                   : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+                   : "v"(p)
+                   : "memory");
+      breg[B][0][0] = t0;
+      breg[B][0][1] = t1;
+      breg[B][1][0] = t2;
+      breg[B][1][1] = t3;
+    };
+    auto a_stage = [&](int kstep) { return lds + (kstep & (kAStages - 1)) * BM * LDS_STRIDE; };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using W12 = std::integral_constant<int, 12>;
+    using W6 = std::integral_constant<int, 6>;
+    using W0 = std::integral_constant<int, 0>;
+    using Yes = std::true_type;
+    using No = std::false_type;
+    // one K step: buffer B of the ring, W loads of later steps allowed in flight,
+    // ISSUE: start the loads of step kt + 3
+    auto step = [&](auto bi, auto wi, auto issue, int kt) __attribute__((always_inline)) {
+      constexpr int B = decltype(bi)::value, W = decltype(wi)::value;
+      if constexpr (W == 12)
+        __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12)
+      else if constexpr (W == 6)
+        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      const uint32_t la = lds_addr(a_stage(kt)) + (lane & 31) * LDS_STRIDE;
+      v4i af[2][MB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t koff = ks ? koff1 : koff0;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) af[ks][mb] = ds_read16(la + mb * 32 * LDS_STRIDE + koff);
+      }
+      if constexpr (decltype(issue)::value) {
+        load_b(std::integral_constant<int, (B + kDepth) % 4>{}, kt + kDepth);
+        dma_a(min(kt + kDepth, KT - 1), a_stage(kt + kDepth));  // padded steps: any valid A
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the A fragments are in registers
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          // 32-row blocks past the slot's rows have nothing to compute; the first
+          // always runs (a tile has rows), so every path consumes the buffer
+          if (mb > 0 && mb >= mb_live) break;
+          acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], breg[B][ks][0], acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], breg[B][ks][1], acc[mb][1], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_b(I0{}, 0);
+    dma_a(0, a_stage(0));
+    load_b(I1{}, 1);
+    dma_a(min(1, KT - 1), a_stage(1));
+    load_b(I2{}, 2);
+    dma_a(min(2, KT - 1), a_stage(2));
+    for (int kt0 = 0; kt0 < KTp - 4; kt0 += 4) {
+      step(I0{}, W12{}, Yes{}, kt0);
+      step(I1{}, W12{}, Yes{}, kt0 + 1);
+      step(I2{}, W12{}, Yes{}, kt0 + 2);
+      step(I3{}, W12{}, Yes{}, kt0 + 3);
+    }
+    step(I0{}, W12{}, Yes{}, KTp - 4);  // starts the loads of the last step
+    step(I1{}, W12{}, No{}, KTp - 3);
+    step(I2{}, W6{}, No{}, KTp - 2);
+    step(I3{}, W0{}, No{}, KTp - 1);  // vmcnt(0): nothing is in flight past this point
   }
   __syncthreads();
 
@@ -589,29 +687,36 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restr
 }
 
 // ------------------------------------------------------- weight packing ---
-// One thread per 16-byte slot of the image: slot j of tile row r in block
-// (e, n, s) is bytes 64 s + 16 (j ^ ((r >> 2) & 3)) .. +16 of that row's
-// weights -- the swizzled LDS order of the GEMM's K step s.
+// One thread per 16-byte slot of the image.  Block (e, n, s) holds, for each
+// wavefront w of the GEMM and each MFMA fragment (ks, nb) of its K step, the
+// 64 lanes' 16-byte operands in lane order: lane l takes tile row
+// col(w, nb) + (l & 31), K bytes 64 s + 32 ks + 16 (l >> 5) .. +16.  Steps
+// past K (the image pads K to whole groups of four steps) are zero.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restrict__ w,
                                                            int gateup, int E, int H, int I,
                                                            int8_t *__restrict__ packed) {
-  const int K = gateup ? H : I, KT = K / BK;
+  const int K = gateup ? H : I, KT = K / BK, KTp = packed_ksteps(K);
   const int NT = packed_ntiles(gateup ? MOE_PROJ_GATEUP : MOE_PROJ_DOWN, H, I);
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q >= (int64_t)E * NT * KT * (kPackedStepBytes / 16)) return;
-  const int j = (int)(q & 3), r = (int)((q >> 2) & 255);
+  if (q >= (int64_t)E * NT * KTp * (kPackedStepBytes / 16)) return;
+  const int l = (int)(q & 63), f = (int)((q >> 6) & 3), wv = (int)((q >> 8) & 3);
+  const int ks = f >> 1, nb = f & 1;
   const int64_t blk = q >> 10;
-  const int s = (int)(blk % KT), n = (int)((blk / KT) % NT);
-  const int64_t e = blk / ((int64_t)KT * NT);
-  const int chunk = j ^ ((r >> 2) & 3);
-  int64_t row;
-  if (gateup) {
-    const int pair = min(n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);
-    row = e * 2 * I + (r < BN / 2 ? pair : I + pair);
-  } else {
-    row = e * H + min(n * BN + r, H - 1);
+  const int s = (int)(blk % KTp), n = (int)((blk / KTp) % NT);
+  const int64_t e = blk / ((int64_t)KTp * NT);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (s < KT) {
+    int64_t row;
+    if (gateup) {  // tile rows: 128 gate pairs, then the 128 matching up rows
+      const int r = nb * (BN / 2) + wv * 32 + (l & 31);
+      const int pair = min(n * (BN / 2) + (r & (BN / 2 - 1)), I - 1);
+      row = e * 2 * I + (r < BN / 2 ? pair : I + pair);
+    } else {
+      row = e * H + min(n * BN + wv * 64 + nb * 32 + (l & 31), H - 1);
+    }
+    v = *(const uint4 *)(w + row * K + (int64_t)s * BK + 32 * ks + 16 * (l >> 5));
   }
-  *(uint4 *)(packed + q * 16) = *(const uint4 *)(w + row * K + (int64_t)s * BK + chunk * 16);
+  *(uint4 *)(packed + q * 16) = v;
 }
 
 }  // namespace

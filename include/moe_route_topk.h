@@ -261,22 +261,25 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
                     void *scratch, size_t scratch_bytes, void *stream);
 
 /*
- * moe_pack_expert_weights -- INT8 expert weights into the expert GEMMs' tile
+ * moe_pack_expert_weights -- INT8 expert weights into the expert GEMMs' operand
  * image [XDS DeepSeek INT8 量化, P088: the routed experts' weights are stored
- * INT8; how they sit in memory is left open].  The image makes the 16 KB of
- * weights that one 256-row GEMM tile consumes per 64-byte K step one
- * contiguous run, already in the order the GEMM stages it in LDS, so each
- * step's weight fetch is whole 128-byte lines.  Run once when the weights are
- * loaded; the GEMMs take only the image.
+ * INT8; how they sit in memory is left open].  In the image, the weights that
+ * each of a GEMM tile's four wavefronts multiplies in one 64-byte K step are 4
+ * KB of consecutive bytes, already in MFMA operand order, so the GEMM loads
+ * them straight into registers as whole 128-byte lines, several steps ahead.
+ * Run once when the weights are loaded; the GEMMs take only the image.
  *   proj MOE_PROJ_GATEUP: w = [E][2I][H] (rows 0..I-1 gate, I..2I-1 up), K = H,
  *     NT = ceil(I / 128) n-tiles of 128 gate/up pairs; tile row r < 128 is gate
  *     row min(128 n + r, I - 1), row r >= 128 is up row I + min(128 n + r - 128, I - 1).
  *   proj MOE_PROJ_DOWN: w = [E][H][I], K = I, NT = ceil(H / 256); tile row r is
  *     row min(256 n + r, H - 1).
- *   Image: packed[e][n][s][r][j] for K steps s < K / 64, tile rows r < 256 and
- *     16-byte slots j < 4: slot j of row r holds bytes 64 s + 16 (j ^ ((r >> 2) & 3))
- *     .. +16 of that weight row.  Size E * NT * (K / 64) * 16384 bytes
- *     (w_gateup_packed_bytes / w_down_packed_bytes of moe_plan_sizes).
+ *   Image: 16 KB blocks (e, n, s) for K steps s < KTp = K / 64 rounded up to a
+ *     multiple of 4 (steps past K / 64 are zero).  Within a block, 16-byte slot
+ *     1024 w + 256 ks + 64 nb + l (w, ks, nb < 2 or 4 as below, lane l < 64)
+ *     holds K bytes 64 s + 32 ks + 16 (l >> 5) .. +16 of tile row
+ *     GATEUP: 128 nb + 32 w + (l & 31),  DOWN: 64 w + 32 nb + (l & 31)
+ *     (w < 4 wavefronts, ks < 2 MFMA K halves, nb < 2 column blocks).
+ *     Size E * NT * KTp * 16384 bytes (w_gateup_packed_bytes / w_down_packed_bytes).
  *   Requirements: E > 0, H a multiple of 128, I a multiple of 64 and <= 16384,
  *     w and packed 16B-aligned and not overlapping, packed_bytes >= the size.
  * Errors: MOE_ERR_INVALID_ARG (NULL, misaligned, bad proj or E),

@@ -128,14 +128,15 @@ def test_int8_returns_and_router_validation():
 
 def test_pack_expert_weights_validation_and_sizes():
     """The weight packer's sizes (one 16 KB block per expert, n-tile and 64-byte
-    K step; partial n-tiles padded) and its host-side argument checks (no launch)."""
+    K step; partial n-tiles padded, K padded to whole groups of four steps) and
+    its host-side argument checks (no launch)."""
     L = moe.lib()
     s = moe.moe_plan_sizes(moe.geom(T=0, H=7168, E=256, P=256, k=1, D=1, Epp=1, S=1, LB=0), 2048)
     assert s.w_gateup_packed_bytes == 256 * 2 * 2048 * 7168
     assert s.w_down_packed_bytes == 256 * 7168 * 2048
     s = moe.moe_plan_sizes(moe.geom(T=0, H=384, E=3, P=3, k=1, D=1, Epp=1, S=1, LB=0), 192)
-    assert s.w_gateup_packed_bytes == 3 * 2 * (384 // 64) * 16384   # two n-tiles of 128 pairs
-    assert s.w_down_packed_bytes == 3 * 2 * (192 // 64) * 16384     # two n-tiles of 256 rows
+    assert s.w_gateup_packed_bytes == 3 * 2 * 8 * 16384   # two n-tiles of 128 pairs, 6 -> 8 K steps
+    assert s.w_down_packed_bytes == 3 * 2 * 4 * 16384     # two n-tiles of 256 rows, 3 -> 4 K steps
     w, pk = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x40000000)
     ok = s.w_gateup_packed_bytes
     G, D = moe.PROJ_GATEUP, moe.PROJ_DOWN

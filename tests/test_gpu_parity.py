@@ -257,29 +257,38 @@ def test_route_selection_edge_cases(E, k, dtype, mode, biased):
 # ---------------------------------------------------------- weight image ---
 
 def _packed_image(w: np.ndarray, gateup: bool, H: int, I: int) -> np.ndarray:
-    """The tile image that moe_pack_expert_weights documents, by numpy indexing:
-    block (e, n, s), tile row r, slot j = bytes 64 s + 16 (j ^ ((r >> 2) & 3)) .. +16
-    of weight row row(n, r) (clamped rows in partial n-tiles)."""
-    r = np.arange(256)
-    if gateup:
-        K, NT = H, (I + 127) // 128
-        pair = np.minimum(np.arange(NT)[:, None] * 128 + (r % 128)[None, :], I - 1)
-        rows = np.where(r[None, :] < 128, pair, I + pair)
-    else:
-        K, NT = I, (H + 255) // 256
-        rows = np.minimum(np.arange(NT)[:, None] * 256 + r[None, :], H - 1)
-    chunk = np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3)                  # [256][4]
-    blocks = []
-    for s in range(K // 64):
-        cols = 64 * s + 16 * chunk[:, :, None] + np.arange(16)[None, None, :]  # [256][4][16]
-        blocks.append(w[:, rows[:, :, None, None], cols[None]])               # [E][NT][256][4][16]
-    return np.stack(blocks, axis=2).reshape(-1)
+    """The operand image that moe_pack_expert_weights documents, by numpy
+    indexing: block (e, n, s), slot 1024 wv + 256 ks + 64 nb + l = K bytes
+    64 s + 32 ks + 16 (l >> 5) .. +16 of tile row row(wv, nb, l); K padded to a
+    multiple of four 64-byte steps with zeros; clamped rows in partial n-tiles."""
+    E = w.shape[0]
+    K = H if gateup else I
+    KT = K // 64
+    KTp = (KT + 3) // 4 * 4
+    NT = (I + 127) // 128 if gateup else (H + 255) // 256
+    out = np.zeros((E, NT, KTp, 4, 2, 2, 64, 16), np.int8)       # e n s wv ks nb l byte
+    l = np.arange(64)
+    for n in range(NT):
+        for wv in range(4):
+            for nb in range(2):
+                if gateup:
+                    r = nb * 128 + wv * 32 + (l & 31)
+                    pair = np.minimum(n * 128 + (r % 128), I - 1)
+                    rows = np.where(r < 128, pair, I + pair)
+                else:
+                    rows = np.minimum(n * 256 + wv * 64 + nb * 32 + (l & 31), H - 1)
+                for s in range(KT):
+                    for ks in range(2):
+                        cols = 64 * s + 32 * ks + 16 * (l >> 5)
+                        out[:, n, s, wv, ks, nb] = w[:, rows[:, None], cols[:, None] + np.arange(16)]
+    return out.reshape(-1)
 
 
 def test_pack_expert_weights_image():
-    """The packed weights are the documented tile image byte for byte, for both
-    projections, with partial n-tiles on both (I = 192 pairs of 128-pair tiles,
-    H = 384 rows of 256-row tiles)."""
+    """The packed weights are the documented operand image byte for byte, for
+    both projections, with partial n-tiles on both (I = 192 pairs of 128-pair
+    tiles, H = 384 rows of 256-row tiles) and K padded to whole groups of four
+    steps (K = 384: 6 -> 8 steps; K = 192: 3 -> 4)."""
     E, H, I = 3, 384, 192
     rng = np.random.default_rng(11)
     wgu = rng.integers(-128, 128, (E, 2 * I, H), dtype=np.int8)

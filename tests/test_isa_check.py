@@ -1,0 +1,74 @@
+"""The build's check of the expert GEMMs' untracked weight loads, on small
+synthetic assembly listings: it must pass a load consumed by an MFMA, and catch
+each way the invariant can break (a touch before consumption, a copy, a reload
+into a pending register, a path that skips the consumer, a load still pending
+at the end), and accept a vmcnt(0) drain."""
+import pytest
+
+from combine_moe_route_topk_amd.isa_check import check_kernel
+
+LOAD = [";;#ASMSTART", "global_load_dwordx4 v[10:13], v[2:3], off", ";;#ASMEND"]
+MFMA = ["v_mfma_i32_32x32x32_i8 v[20:35], v[40:43], v[10:13], v[20:35]"]
+END = ["s_endpgm"]
+
+
+def bad(lines):
+    return check_kernel("k", lines)
+
+
+def test_consumed_by_mfma_is_clean():
+    assert bad(LOAD + ["v_add_u32_e32 v5, v6, v7"] + MFMA + ["v_mov_b32_e32 v10, 0"] + END) == []
+
+
+def test_touch_before_consumption():
+    assert bad(LOAD + ["v_add_u32_e32 v11, v6, v7"] + MFMA + END)
+    assert bad(LOAD + ["v_mov_b32_e32 v50, v12"] + MFMA + END)          # a copy reads it early
+    assert bad(LOAD + ["scratch_store_dword off, v13, s0"] + MFMA + END)  # a spill
+
+
+def test_mfma_writing_a_pending_register():
+    assert bad(LOAD + ["v_mfma_i32_32x32x32_i8 v[10:25], v[40:43], v[44:47], v[10:25]"] + END)
+
+
+def test_reload_before_consumption_and_address_clobber():
+    assert bad(LOAD + LOAD + MFMA + END)
+    assert bad(LOAD + [";;#ASMSTART", "global_load_dwordx4 v[60:63], v[12:13], off", ";;#ASMEND"]
+               + MFMA + ["v_mfma_i32_32x32x32_i8 v[20:35], v[40:43], v[60:63], v[20:35]"] + END)
+
+
+def test_branch_that_skips_the_consumer():
+    lines = LOAD + ["s_cbranch_scc1 .LBB0_2"] + MFMA + [".LBB0_2:", "v_mov_b32_e32 v10, 0"] + END
+    assert bad(lines)
+
+
+def test_pending_at_end_and_vmcnt_drain():
+    assert bad(LOAD + END)
+    assert bad(LOAD + ["s_waitcnt vmcnt(0)", "v_mov_b32_e32 v10, 0"] + END) == []
+
+
+def test_loop_carried_ring():
+    # a loop that consumes the buffer loaded in the previous iteration, then reloads it
+    ok = LOAD + [".LBB0_1:"] + MFMA + LOAD + ["s_cbranch_scc1 .LBB0_1", "s_waitcnt vmcnt(0)"] + END
+    assert bad(ok) == []
+    broken = LOAD + [".LBB0_1:", "v_mov_b32_e32 v10, 0"] + MFMA + LOAD + ["s_cbranch_scc1 .LBB0_1",
+                                                                        "s_waitcnt vmcnt(0)"] + END
+    assert bad(broken)
+
+
+@pytest.mark.parametrize("n", [1])
+def test_the_built_kernels_have_weight_loads_to_check(n, tmp_path):
+    """The real expert GEMMs, compiled to assembly: weight loads present, no violation."""
+    import os
+    import subprocess
+    from combine_moe_route_topk_amd import build as B
+    from combine_moe_route_topk_amd.isa_check import check_asm
+    if not os.path.exists(B.HIPCC):
+        pytest.skip("needs hipcc")
+    asm = str(tmp_path / "k.s")
+    flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
+    subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-o", asm,
+                    os.path.join(B.PKG, "csrc", "ffn_q8.hip"), "-I", os.path.join(B.ROOT, "include")],
+                   check=True, capture_output=True)
+    text = open(asm).read()
+    assert text.count("global_load_dwordx4") >= 6 * 16   # six GEMM variants, 16+ loads each
+    assert check_asm(asm) == []
