@@ -121,6 +121,10 @@ def check_kernel(name: str, lines) -> list:
     ins = _instructions(lines)
     if not any(a and t.startswith("global_load_dwordx4") for t, a in ins):
         return []
+    # the control-flow graph below knows direct branches only
+    for t, _ in ins:
+        if t.startswith(("s_setpc", "s_swappc", "s_getpc", "s_cbranch_join", "s_call")):
+            return [f"{name}: '{t}': indirect control flow, not analysed"]
     blocks, succ = _blocks(ins)
     state_in = [None] * len(blocks)
     state_in[0] = frozenset()

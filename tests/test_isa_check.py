@@ -46,6 +46,10 @@ def test_pending_at_end_and_vmcnt_drain():
     assert bad(LOAD + ["s_waitcnt vmcnt(0)", "v_mov_b32_e32 v10, 0"] + END) == []
 
 
+def test_indirect_control_flow_is_refused():
+    assert bad(LOAD + ["s_setpc_b64 s[0:1]"] + MFMA + END)
+
+
 def test_loop_carried_ring():
     # a loop that consumes the buffer loaded in the previous iteration, then reloads it
     ok = LOAD + [".LBB0_1:"] + MFMA + LOAD + ["s_cbranch_scc1 .LBB0_1", "s_waitcnt vmcnt(0)"] + END
