@@ -798,12 +798,14 @@ def test_layer_refuses_mismatched_tensors():
 
 def test_expert_gemm_slot_size_boundaries():
     """The grouped GEMMs called directly, one launch over slots of 0, 1, 31, 32, 33,
-    127, 128, 129, 255, 256 and 257 rows (the edges of the 32-row MFMA blocks and
-    the 128-row m-tiles), rows gathered from a shuffled dispatch buffer, slots
+    127, 128, 129, 255, 256, 257 and 1025 rows (the edges of the 32-row MFMA blocks
+    and the 128-row m-tiles; 1025 rows make a full group of eight m-tiles and a
+    lone ninth, whose weights load non-temporal), rows gathered from a shuffled
+    dispatch buffer, slots
     mapped to logical experts out of order, a half-full gate/up n-tile (I = 192)
     and a half-full down n-tile (H = 384): both projections' int32 accumulators
     and the bf16 return rows bit-exact against the oracle, slot by slot."""
-    counts = np.array([0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257], np.int32)
+    counts = np.array([0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1025], np.int32)
     P = E = len(counts)
     H, I = 384, 192
     R = int(counts.sum())
