@@ -18,16 +18,19 @@
 //            epilogue: y = bf16((f32(acc) * hs) * s_down) into the dense
 //            return rows.
 // Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
-// each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes moved global -> LDS by
-// DMA into a ring of three stages, two steps ahead, XOR-swizzled rows.  The
-// weights come pre-packed (moe_pack_expert_weights) in MFMA fragment order:
-// each wavefront loads its own 64 columns of a K step straight into
-// registers, 4 KB as four contiguous 1 KB runs of whole cache lines, three
-// steps ahead of the MFMAs; A alone goes through the LDS ring.  The
-// work list is ordered slot-major, then groups of kGroupM m-tiles, then
-// n-tiles, then m inside the group, and blocks are remapped so that each XCD
-// walks one contiguous stretch of it: the m-tiles of a group share every
-// weight tile in that XCD's L2.
+// each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes.  The A rows move
+// global -> LDS by DMA into a ring of four stages, three steps ahead,
+// XOR-swizzled rows.  The weights come pre-packed (moe_pack_expert_weights) in
+// MFMA fragment order: each wavefront loads its own 64 columns of a K step
+// straight into a ring of four register buffers, 4 KB as four contiguous 1 KB
+// runs of whole cache lines, also three steps ahead of the MFMAs.  The work
+// list is ordered slot-major, then groups of kGroupM m-tiles, then n-tiles,
+// then m inside the group, and blocks are remapped so that each XCD walks one
+// contiguous stretch of it: the m-tiles of a group share every weight tile in
+// that XCD's L2.  Weight tiles that only one block reads, and the outputs,
+// move as non-temporal accesses so that they do not evict the shared tiles.
+// (The gate logits, a bf16 GEMM in the same kernel, keep a three-stage LDS
+// ring for both operands, two steps ahead.)
 #include <type_traits>
 
 #include "common.h"
@@ -49,7 +52,9 @@ constexpr int LDS_STRIDE = BK;  // bytes per LDS row
 // four rows x four chunks) and the MFMA operand reads (16 lanes = sixteen rows,
 // one chunk: rows r, r+4, r+8, r+12 would share banks without it).
 constexpr int kGroupM = 8;
-constexpr int kStages = 3;  // LDS ring depth: the DMA runs two K steps ahead
+// LDS arena: three stages of (A + B) rows -- the gate logits' ring, DMA two K
+// steps ahead; the INT8 projections hold their four A stages in it
+constexpr int kStages = 3;
 // epilogue staging: 128 fp32 per row + 8 pad (rows 4 apart land 32 banks apart)
 constexpr int kStageStride = 128 + 8;
 // bf16 staging of the down projection: 256 bf16 per row + 32 B pad
@@ -137,10 +142,9 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 //              epilogue: bf16 return rows.
 // Block tile 128 x 256, four wavefronts side by side along N, each owning all
 // 128 rows x 64 columns (4 x 2 MFMA 32x32 blocks, 128 accumulators): the four
-// waves share every A fragment read from LDS, which keeps LDS reads at 6 KB per
-// 32-wide K sub-step per wave.  The DMA of step kt + 2 is in flight while
-// step kt feeds the MFMAs from LDS; one barrier per K step; two blocks per CU
-// overlap each other's waits.
+// waves share every A fragment read from LDS.  The loads of step kt + 3 are in
+// flight while step kt feeds the MFMAs (kt + 2 in ROUTER mode); one barrier
+// per K step; two blocks per CU overlap each other's waits.
 // Q8OUT (DOWN only): the return rows are INT8 with one fp32 scale per 256
 // columns (the n-tile) instead of bf16 -- see the epilogue.
 template <int MODE, bool DBG, bool Q8OUT = false>
