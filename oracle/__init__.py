@@ -15,7 +15,10 @@ from typing import Optional
 import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_DIR, "libmoe_oracle.so")
+# MOE_ORACLE_LIB points the tests at another build of moe_oracle.c (the
+# mutation test builds copies with planted mistakes and checks that the pins
+# reject each of them)
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_DIR, "libmoe_oracle.so")
 _lib = None
 
 _P = ctypes.c_void_p

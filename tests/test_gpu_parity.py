@@ -724,6 +724,33 @@ def test_single_token_and_zero_token():
     assert np.all(host(c.layer.buf.out)[2] == 0)
 
 
+def test_dispatch_quantization_special_tokens():
+    """fp32 tokens at the edges of the token-wise INT8 rule, bit-exact against
+    the oracle: subnormal tokens whose scale underflows to 2^-149 so that the
+    clamp to +-127 decides the codes (both signs of the amax element), an
+    all-zero token, exact halves at scale 1 (round half to even), signed zeros
+    with tiny normals, and values near the top of the fp32 range."""
+    w = mw.WORKLOADS["tiny"]
+    c = Case(w)
+    rng = np.random.default_rng(31)
+    m = rng.integers(-150, 151, w.H)
+    m[0], m[1] = 150, -149
+    c.x[0] = m.astype(np.float32) * np.float32(2.0 ** -149)
+    c.x[1] = -c.x[0]
+    c.x[2] = 0.0
+    c.x[3] = 0.5 + rng.integers(-127, 127, w.H).astype(np.float32)
+    c.x[3, :3] = [127.0, 2.5, -2.5]
+    c.x[4] = np.where(rng.random(w.H) < 0.5, np.float32(-0.0),
+                      rng.standard_normal(w.H).astype(np.float32) * np.float32(1e-37))
+    c.x[5] = rng.uniform(-3e38, 3e38, w.H).astype(np.float32)
+    c.x_d = dev_bits(c.x, False)
+    _, _, phys = _check_route(c)
+    q, s, _ = _check_dispatch(c, phys)
+    assert s[0] == np.float32(2.0 ** -149) and q[0, 0] == 127 and q[1, 0] == -127
+    assert s[2] == 0 and np.all(q[2] == 0)
+    assert s[3] == 1 and q[3, :3].tolist() == [127, 2, -2]
+
+
 def test_invalid_routes_are_flagged_not_written():
     """Out-of-range physical ids are dropped (row indices -1) and reported in the
     device status word; nothing is written out of bounds."""

@@ -182,10 +182,18 @@ def test_quant_half_even_closed_form():
 def test_quant_matches_library_rounding_and_bounds():
     """torch.round (half to even) of x / s with s = amax / 127 in fp32 gives the
     same codes; |x - q s| <= s (0.5 + 2^-16); the amax element maps to +-127;
-    an all-zero token gives s = 0, q = 0; bf16 input decodes exactly."""
+    an all-zero token gives s = 0, q = 0; bf16 input decodes exactly.
+    Rows 8 and 9 are subnormal tokens (integers m times 2^-149, |m| <= 150):
+    s = fl(amax / 127) rounds to 2^-149, x / s = m, and the clamp is what keeps
+    the codes in [-127, 127] (the amax element still maps to +-127; the
+    half-step error bound does not hold there and is checked on the other rows)."""
     rng = np.random.default_rng(4)
     x = rng.standard_normal((64, 256)).astype(np.float32) * rng.uniform(1e-3, 1e3, (64, 1)).astype(np.float32)
     x[7] = 0.0
+    m = rng.integers(-150, 151, 256)
+    m[0], m[1] = 150, -150
+    x[8] = m.astype(np.float32) * np.float32(2.0 ** -149)
+    x[9] = -x[8]
     xb = mw.to_bf16_bits(x)
     for arr, is_bf16, xf in ((x, False, x), (xb, True, _bf16_to_f32(xb))):
         q, s = oracle.quant_tokens(arr, is_bf16)
@@ -201,8 +209,13 @@ def test_quant_matches_library_rounding_and_bounds():
         i = np.abs(xf).argmax(1)
         rows = np.arange(64)[nz.numpy()]
         assert np.all(np.abs(q[rows, i[rows]]) == 127)
-        err = np.abs(xf.astype(np.float64) - q.astype(np.float64) * s[:, None])
-        assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 2.0 ** -16))
+        assert q.min() >= -127
+        if not is_bf16:  # bf16 cannot hold the subnormal rows (they round to zero tokens)
+            assert s[8] == np.float32(2.0 ** -149) and q[8].tolist() == np.clip(m, -127, 127).tolist()
+            assert q[9].tolist() == np.clip(-m, -127, 127).tolist()
+        normal = np.setdiff1d(np.arange(64), [8, 9])
+        err = np.abs(xf[normal].astype(np.float64) - q[normal].astype(np.float64) * s[normal, None])
+        assert np.all(err <= s[normal, None].astype(np.float64) * (0.5 + 2.0 ** -16))
 
 
 # ---------------------------------------------------- c4 dispatch layout ---
@@ -264,10 +277,14 @@ def test_dispatch_layout_library_pins(S, LB, D, Epp, k):
 
 def test_dispatch_capacity_error():
     """A partition with more slots than declared can receive more than
-    cap = LB min(k, Epp) routes from one source: the oracle reports capacity."""
+    cap = LB min(k, Epp) routes from one source: the oracle reports capacity
+    from the first route past cap (cap + 1 routes fail, cap routes fit)."""
     w = _small_workload(T=8, S=1, LB=8, D=2, Epp=1, P=4, E=4, k=2)
-    phys = np.tile(np.array([0, 1], np.int32), (8, 1))
     sp = np.array([0, 0, 1, 1], np.int32)  # two slots on partition 0 but Epp = 1
+    # cap = 8: every token's first route goes to partition 0; token 5's second too
+    phys = np.tile(np.array([0, 2], np.int32), (8, 1))
+    assert oracle.dispatch_layout(w, phys, sp, 1)["meta"][0, 0, 2] == 8
+    phys[5, 1] = 1
     with pytest.raises(oracle.OracleError) as ei:
         oracle.dispatch_layout(w, phys, sp, 1)
     assert ei.value.rc == -3
@@ -391,6 +408,28 @@ def test_combine_against_float64_einsum_and_unit_weight():
 
 # ----------------------------------------- c6' INT8 returns (block scales) ---
 
+def test_combine_bf16_output_equals_library_rounding():
+    """k = 1, weight 1: the bf16 output is the fp32 value q * s rounded to bf16,
+    which must equal torch's float32 -> bfloat16 conversion (round to nearest,
+    ties to even) -- including exact ties such as 1 + 2^-8 and 3 + 2^-7, and
+    values of every magnitude."""
+    rng = np.random.default_rng(21)
+    H = 64
+    sc = np.concatenate([np.float32([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1.5 + 2.0 ** -8]),
+                         rng.uniform(0.5, 2.0, 125).astype(np.float32)
+                         * np.float32(2.0) ** rng.integers(-60, 60, 125).astype(np.float32)])
+    q = rng.integers(-127, 128, (sc.size, H)).astype(np.int8)
+    q[:3, :4] = [1, 2, 3, -1]
+    rows = np.zeros((sc.size, H + 16), np.uint8)
+    rows[:, :H] = q.view(np.uint8)
+    rows[:, H:H + 4] = sc.view(np.uint8).reshape(-1, 4)
+    rr = np.arange(sc.size, dtype=np.int32).reshape(-1, 1)
+    out = oracle.combine(rows, rr, np.ones((sc.size, 1), np.float32), 1, H, "q8", True, scale_offset=H)
+    v = torch.from_numpy(q.astype(np.float32) * sc[:, None])
+    ref = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, ref)
+
+
 def test_quant_blocks_equal_token_rule_per_block():
     """XDS P089 (outputs quantized to INT8 before they travel): each 256-column
     block of a row, partial last block included, gets exactly the codes and
@@ -494,8 +533,45 @@ def test_eplb_plan_invariants_on_skewed_counts():
                 best = (tl, cand)
         assert best[1] == c
         copies[c] += 1
-    # replicas go to the free slots (partitions E..E+budget-1), heaviest first
-    assert sorted(out["slot_partition"][E:].tolist()) == list(range(E, E + budget))
+    # replicas go to the free slots (partitions E..E+budget-1), which all start
+    # empty: the heaviest replica takes the lowest partition id, and so on up
+    # (SELECT_AND_PLACE_REPLICAS sorts by load; ties of partition load go to
+    # the lower id), which reproduces the single-slot placement 256, 257, ...
+    order = sorted(range(budget), key=lambda i: (-cnt.sum(0)[out["selected"][i]], i))
+    placed = [int(out["slot_logical"][E + i]) for i in range(budget)]
+    assert placed == [int(out["selected"][i]) for i in order]
+    assert out["slot_partition"][E:].tolist() == list(range(E, E + budget))
+
+
+def test_eplb_plan_candidate_tie_rules_worked():
+    """Hand-worked: one slice, counts (3, 10, 10), one redundant slot.  The
+    candidates are the slices' hottest experts, the lower id on a tie, so the
+    only candidate is expert 1; its extra copy leaves the tail at 10 (expert 2
+    still carries 10).  Expert 1 is selected -- neither the higher-id tied
+    expert 2 nor expert 0, which gives the same tail but is no slice's hottest
+    (XDS 专家负载均衡, SELECT_AND_PLACE_REPLICAS)."""
+    out = oracle.eplb_plan(np.array([[3, 10, 10]]), 1, 2, np.array([0, 0, 1]), np.array([0, 1]))
+    assert out["selected"].tolist() == [1]
+    np.testing.assert_allclose(out["tail"], [10.0, 10.0])
+    assert out["slot_logical"].tolist() == [0, 1, 2, 1]
+    assert out["slot_partition"].tolist() == [0, 0, 1, 1]
+
+
+def test_eplb_plan_primary_shares_worked():
+    """Hand-worked placement where replicas may share a partition with primaries:
+    one slice, counts (100, 10, 60, 45), primaries {0, 1} on partition 0 and
+    {2, 3} on partition 1, one free slot on each, one redundant slot.  Expert 0
+    is the hottest and gets the copy (tail 100 -> 60).  A primary's partition
+    carries total / copies: partition 0 holds 100/2 + 10 = 60 and partition 1
+    holds 60 + 45 = 105, so the replica (load 50) goes to partition 0."""
+    out = oracle.eplb_plan(np.array([[100, 10, 60, 45]]), 1, 2, np.array([0, 0, 1, 1]),
+                           np.array([1, 1]))
+    assert out["selected"].tolist() == [0]
+    np.testing.assert_allclose(out["tail"], [100.0, 60.0])
+    assert out["slot_partition"].tolist() == [0, 0, 1, 1, 0]
+    assert out["slot_logical"].tolist() == [0, 1, 2, 3, 0]
+    assert out["replica_offsets"].tolist() == [0, 2, 3, 4, 5]
+    assert out["replica_slots"].tolist() == [0, 4, 1, 2, 3]
 
 
 # ---------------------------------------------------------- c4' sizes ---
