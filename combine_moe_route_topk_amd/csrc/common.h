@@ -27,10 +27,13 @@ inline int router_splits(const moe_geom_t &g) {
 inline int64_t router_scratch_bytes_of(const moe_geom_t &g) {
   return (int64_t)router_splits(g) * g.T * g.E * 4;
 }
-// INT8 return row: H codes, then one fp32 scale per MOE_RET_Q8_BLOCK columns, 16-byte rows
+// INT8 return row: H codes, then one fp32 scale per MOE_RET_Q8_BLOCK columns.
+// Rows are whole 128-byte cache lines, so that every 256-column block of codes
+// a GEMM tile stores covers whole lines (a row of H + 4 nblk bytes rounded only
+// to 16 would leave most blocks straddling lines, written partially by two tiles)
 inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
   const int64_t nblk = ((int64_t)g.H + MOE_RET_Q8_BLOCK - 1) / MOE_RET_Q8_BLOCK;
-  return ((int64_t)g.H + 4 * nblk + 15) / 16 * 16;
+  return ((int64_t)g.H + 4 * nblk + 127) / 128 * 128;
 }
 
 // Image of the INT8 expert weights (moe_pack_expert_weights): one 16 KB block

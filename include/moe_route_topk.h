@@ -124,7 +124,8 @@ typedef struct moe_sizes {
                                        /* when relays > 0 (E2A staging follows the rows)  */
   int64_t dispatch_scratch_bytes;      /* scratch of moe_dispatch_q8                      */
   int64_t ffn_scratch_bytes;           /* scratch of moe_expert_ffn_q8 (I > 0)            */
-  int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256), 16B   */
+  int64_t ret_q8_row_bytes;            /* one INT8 return row: H + 4 ceil(H / 256) bytes  */
+                                       /* rounded up to whole 128-byte lines              */
   int64_t ret_q8_bytes;                /* T * k INT8 return rows                          */
   int64_t router_scratch_bytes;        /* scratch of moe_router_logits / moe_router_topk  */
   int64_t w_gateup_packed_bytes;       /* moe_pack_expert_weights image, MOE_PROJ_GATEUP  */
@@ -352,7 +353,9 @@ int moe_expert_down_q8(const int32_t *slot_count, const int32_t *slot_offset,
  *   s = max |y| over the block / 127,  q = clamp(round_half_even(y / s), +-127)
  *   (fp32 divisions; an all-zero block gives s = 0, q = 0).
  *   ret_q8  [T*k][ret_q8_row_bytes] (moe_plan_sizes): row slot_offset[p] + i
- *           holds H int8 codes, then ceil(H / 256) fp32 scales; 16B.
+ *           holds H int8 codes, then ceil(H / 256) fp32 scales, then padding
+ *           to a whole number of 128-byte lines; 16B (a 128-byte aligned
+ *           buffer keeps every 256-column block of codes on whole lines).
  * Combine these rows with mode MOE_RET_Q8_BLOCKS.  Geometries with relays are
  * not supported (MOE_ERR_UNSUPPORTED): the E2A hop moves bf16 rows.
  * Other arguments, preconditions and errors as moe_expert_down_q8.

@@ -100,8 +100,10 @@ def test_int8_returns_and_router_validation():
     fake = ctypes.c_void_p(0x1000)
     g = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
     s = moe.moe_plan_sizes(g, 256)
-    # INT8 return rows: H codes + one fp32 scale per 256 columns, 16-byte rows
-    assert s.ret_q8_row_bytes == 256 + 16 and s.ret_q8_bytes == 16 * 2 * 272
+    # INT8 return rows: H codes + one fp32 scale per 256 columns, whole 128-byte lines
+    assert s.ret_q8_row_bytes == 384 and s.ret_q8_bytes == 16 * 2 * 384
+    g2 = moe.geom(T=16, H=7168, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    assert moe.moe_plan_sizes(g2, 256).ret_q8_row_bytes == 7296  # 7168 + 112 -> 57 lines
     relay = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=1, S=4, LB=4, relays=2)
     assert L.moe_expert_down_q8_int8ret(fake, fake, fake, fake, fake, 256, ctypes.byref(relay),
                                         fake, None, fake, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED

@@ -579,7 +579,7 @@ def test_expert_int8_returns_and_combine_small():
     n = w.T * w.k
     b = c.layer.buf
     rb = b.sizes.ret_q8_row_bytes
-    assert rb == ((w.H + 4 * 2 + 15) // 16) * 16
+    assert rb == ((w.H + 4 * 2 + 127) // 128) * 128  # codes, two block scales, whole lines
     acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
     c.layer.experts_gateup()
     c.layer.experts_down_int8ret(acc_d)
