@@ -603,24 +603,29 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
           const uint4 *src = (const uint4 *)((const uint8_t *)stb + lr * kStageStrideB + c16 * 2);
           const uint4 a = src[0], b = src[1];
           const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          uint32_t pk[4] = {0, 0, 0, 0};
+          // code + 128 = median(rint(q) + 128, 1, 255) (exact: small integers),
+          // converted into its byte by v_cvt_pk_u8_f32; the final xor with
+          // 0x80 per byte turns code + 128 back into the int8 code
+          uint32_t pk[4] = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};  // code 0
+          auto put = [&](int e, float q) __attribute__((always_inline)) {
+            const float t = __builtin_amdgcn_fmed3f(rintf(q) + 128.0f, 1.0f, 255.0f);
+            pk[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(t, e & 3, pk[e >> 2]);
+          };
+          auto y_of = [&](int e) __attribute__((always_inline)) {
+            return bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          };
+          if (sq != 0.0f && rq != 0.0f) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float y = bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-            int code = 0;
-            if (sq != 0.0f) {
-              float q;
-              if (rq != 0.0f) {
-                const float q0 = y * rq;
-                q = fmaf(fmaf(-q0, sq, y), rq, q0);
-              } else {
-                q = y / sq;
-              }
-              code = (int)fminf(fmaxf(rintf(q), -127.0f), 127.0f);
+            for (int e = 0; e < 16; ++e) {
+              const float y = y_of(e), q0 = y * rq;
+              put(e, fmaf(fmaf(-q0, sq, y), rq, q0));
             }
-            pk[e >> 2] |= ((uint32_t)code & 0xffu) << (8 * (e & 3));
+          } else if (sq != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) put(e, y_of(e) / sq);
           }
-          const v4i codes = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+          const v4i codes = {(int)(pk[0] ^ 0x80808080u), (int)(pk[1] ^ 0x80808080u),
+                             (int)(pk[2] ^ 0x80808080u), (int)(pk[3] ^ 0x80808080u)};
           __builtin_nontemporal_store(codes, (v4i *)(retq + rr * ret_row_bytes + n0 + c16));
         }
       }
