@@ -562,7 +562,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       // returns; each row's 256 columns (one block) get the token rule --
       // amax over the block, s = amax / 127, q = clamp(rne(y / s), +-127).
       // Columns past H staged 0, so they do not move the amax.  Row layout:
-      // H codes, then ceil(H / 256) fp32 block scales.
+      // H codes, then ceil(H / 256) fp32 block scales, padded to whole 128-byte
+      // lines (so each block of codes a tile stores is two whole lines).
       // The quotient y / s is taken without a division per element: with the
       // row's r = 1 / s (one IEEE division), q0 = y r, e = fma(-q0, s, y) and
       // q = fma(e, r, q0) (Markstein's correction step).  For s >= 2^-100 this
