@@ -55,9 +55,11 @@ constexpr int kGroupM = 8;
 // LDS arena: three stages of (A + B) rows -- the gate logits' ring, DMA two K
 // steps ahead; the INT8 projections hold their four A stages in it
 constexpr int kStages = 3;
-// epilogue staging: 128 fp32 per row + 8 pad (rows 4 apart land 32 banks apart)
+// epilogue staging: fp32 rows of 128 + 8 values (the row scans' 16 lanes, 8
+// rows x 2 float4 columns, land on distinct bank groups; a stride of 128 + 4
+// spreads the staging writes further but conflicts there, and measured slower)
+// and bf16 rows of 256 values + 32 bytes
 constexpr int kStageStride = 128 + 8;
-// bf16 staging of the down projection: 256 bf16 per row + 32 B pad
 constexpr int kStageStrideB = 2 * 256 + 32;
 static_assert(128 * kStageStride * 4 <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
 static_assert(128 * kStageStrideB <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
@@ -416,8 +418,10 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
           // 32-row blocks past the slot's rows have nothing to compute; the first
           // always runs (a tile has rows), so every path consumes the buffer
           if (mb > 0 && mb >= mb_live) break;
-          acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], breg[B][ks][0], acc[mb][0], 0, 0, 0);
-          acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], breg[B][ks][1], acc[mb][1], 0, 0, 0);
+          // weights as the first operand: the accumulators come out with
+          // token rows across lanes and output columns across registers
+          acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[B][ks][0], af[ks][mb], acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[B][ks][1], af[ks][mb], acc[mb][1], 0, 0, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -452,11 +456,12 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 
 
   // ------------------------------------------------------------ epilogue ---
-  // acc[mb][nb][r] holds tile row mb*32 + 8*(r/4) + 4*(lane/32) + r%4 and
-  // column (lane % 32) of the wave's nb-th 32-column block.  Results go through
-  // an fp32 LDS staging tile [128 rows][128 columns] (row stride kStageStride,
-  // padded so the two lane halves hit different banks) and leave as 16-byte
-  // vector stores.
+  // GATEUP, DOWN: acc[mb][nb][r] holds token row mb*32 + (lane % 32) and
+  // column 8*(r/4) + 4*(lane/32) + r%4 of the wave's nb-th 32-column block
+  // (the weights are the MFMA's first operand).  Results go through an LDS
+  // staging tile (fp32 h [128][128], or bf16 [128][256]), each lane writing
+  // its runs of four consecutive columns at once, and leave as 16-byte vector
+  // stores of whole rows.  ROUTER keeps the other operand order: see there.
   const int col = lane & 31, half = lane >> 5;
   if constexpr (MODE == ROUTER) {
     // partial logits of this K split: acc[mb][nb][r] is tile row
@@ -477,31 +482,46 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     return;
   } else {
   float *stg = (float *)lds;
-  auto stage_put = [&](int lr, int sc, float v) { stg[lr * kStageStride + sc] = v; };
   if (MODE == GATEUP) {
-    const int n = tl.n * (BN / 2) + wave * 32 + col;  // gate / up pair index
-    const bool nok = n < I;
-    const float sg = nok ? wscale[(int64_t)e * 2 * I + n] : 0.0f;
-    const float su = nok ? wscale[(int64_t)e * 2 * I + I + n] : 0.0f;
+    // acc[mb][0][r] / acc[mb][1][r]: gate / up of token row mb*32 + col and of
+    // pair wave*32 + 8*(r/4) + 4*half + r%4 of the tile -- four runs of four
+    // consecutive pairs, each staged by one 16-byte LDS write
+    const int nw = tl.n * (BN / 2) + wave * 32 + 4 * half;  // + 8 g + q: pair index
+    float sgv[4][4], suv[4][4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int n = nw + 8 * g4;  // I % 64 == 0: a run is all below I or all past it
+      const float4 a = n < I ? *(const float4 *)(wscale + (int64_t)e * 2 * I + n)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = n < I ? *(const float4 *)(wscale + (int64_t)e * 2 * I + I + n)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      sgv[g4][0] = a.x; sgv[g4][1] = a.y; sgv[g4][2] = a.z; sgv[g4][3] = a.w;
+      suv[g4][0] = b.x; suv[g4][1] = b.y; suv[g4][2] = b.z; suv[g4][3] = b.w;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      const int lr = mb * 32 + col;
+      const int64_t rr = row0 + lr;
+      const float sx = row_scale[lr];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int64_t rr = row0 + lr;
-        const bool ok = nok && lr < rows_here && rr < nrows;
-        const int32_t ag = acc[mb][0][r], au = acc[mb][1][r];
-        const float sx = row_scale[lr];
-        const float g = ((float)ag * sx) * sg;
-        const float u = ((float)au * sx) * su;
-        const float ex = (float)exp(-(double)g);
-        const float hv = (g / (1.0f + ex)) * u;
-        // columns past I stage 0 (g = u = 0), so the row scans below see only real h
-        stage_put(lr, wave * 32 + col, hv);
-        if (DBG && ok) {
-          acc_dbg[rr * 2 * I + n] = ag;
-          acc_dbg[rr * 2 * I + I + n] = au;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t ag = acc[mb][0][4 * g4 + q], au = acc[mb][1][4 * g4 + q];
+          const float g = ((float)ag * sx) * sgv[g4][q];
+          const float u = ((float)au * sx) * suv[g4][q];
+          const float ex = (float)exp(-(double)g);
+          hv[q] = (g / (1.0f + ex)) * u;
+          const int n = nw + 8 * g4 + q;
+          if (DBG && n < I && lr < rows_here && rr < nrows) {
+            acc_dbg[rr * 2 * I + n] = ag;
+            acc_dbg[rr * 2 * I + I + n] = au;
+          }
         }
+        // pairs past I stage 0 (g = u = 0), so the row scans below see only real h
+        *(float4 *)(stg + lr * kStageStride + wave * 32 + 4 * half + 8 * g4) =
+            make_float4(hv[0], hv[1], hv[2], hv[3]);
       }
     }
     __syncthreads();
@@ -534,24 +554,40 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     }
   } else {
     // bf16 staging [128 rows][256 columns] (row stride kStageStrideB bytes),
-    // converted before staging, so the stored bits are the same
+    // converted before staging, so the stored bits are the same.
+    // acc[mb][nb][r]: token row mb*32 + col, tile column
+    // wave*64 + nb*32 + 8*(r/4) + 4*half + r%4 -- four runs of four columns,
+    // each staged by one 8-byte LDS write
     const int n0 = tl.n * BN;
     uint16_t *stb = (uint16_t *)lds;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int sc = wave * 64 + nb * 32 + col;  // tile column
-      const int c = n0 + sc;
-      const float sd = c < H ? wscale[(int64_t)e * H + c] : 0.0f;
+      const int sb = wave * 64 + nb * 32 + 4 * half;  // + 8 g + q: tile column
+      float sdv[4][4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = n0 + sb + 8 * g4;  // H % 128 == 0: a run is all below H or all past it
+        const float4 v = c < H ? *(const float4 *)(wscale + (int64_t)e * H + c)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        sdv[g4][0] = v.x; sdv[g4][1] = v.y; sdv[g4][2] = v.z; sdv[g4][3] = v.w;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        const int lr = mb * 32 + col;
+        const int64_t rr = row0 + lr;
+        const float hsr = row_scale[lr];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int32_t a = acc[mb][nb][r];
-          stb[lr * (kStageStrideB / 2) + sc] =
-              (uint16_t)f32_to_bf16_bits(((float)a * row_scale[lr]) * sd);
-          const int64_t rr = row0 + lr;
-          if (DBG && lr < rows_here && rr < nrows && c < H) acc_dbg[rr * H + c] = a;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint32_t b[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int32_t a = acc[mb][nb][4 * g4 + q];
+            b[q] = f32_to_bf16_bits(((float)a * hsr) * sdv[g4][q]);
+            const int c = n0 + sb + 8 * g4 + q;
+            if (DBG && lr < rows_here && rr < nrows && c < H) acc_dbg[rr * H + c] = a;
+          }
+          *(uint2 *)(stb + lr * (kStageStrideB / 2) + sb + 8 * g4) =
+              make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
         }
       }
     }
