@@ -6,6 +6,8 @@ is then the same IEEE expression on both sides, so the gate/up outputs, and the
 requantized hq, hs that feed the down projection, are bit-equal for any input
 exactly when the two exponentials agree.  ``exp_exhaustive.hip`` (built by
 ``__graft_entry__.build()``) checks all 4,278,190,082 non-NaN fp32 inputs.
+The file name sorts last so that a failure here never stops the parity tests
+of a ``pytest -x`` run before they have run.
 """
 import os
 import subprocess
