@@ -849,7 +849,9 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   if (!disp_buf || !slot_count || !slot_offset || !slot_rows || !slot_logical || !w_gateup ||
       !s_gateup)
     return MOE_ERR_INVALID_ARG;
-  if (!aligned16(disp_buf) || !aligned16(w_gateup)) return MOE_ERR_INVALID_ARG;
+  // the epilogue reads the channel scales four at a time (16-byte loads)
+  if (!aligned16(disp_buf) || !aligned16(w_gateup) || !aligned16(s_gateup))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->tiles);
   if ((st = launch_status()) != MOE_OK) return st;
@@ -884,7 +886,7 @@ int expert_down(const int32_t *slot_count, const int32_t *slot_offset,
   if (a->nrows == 0) return MOE_OK;
   if (!slot_count || !slot_offset || !slot_logical || !w_down || !s_down || !ret)
     return MOE_ERR_INVALID_ARG;
-  if (!aligned16(w_down) || !aligned16(ret)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_down) || !aligned16(s_down) || !aligned16(ret)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ffn_requant_kernel, dim3((unsigned)((a->nrows + 3) / 4)), dim3(256), 0, s,
                      a->h, a->pmax, slot_offset, g->P, I, a->nrows, a->hq, a->hs);

@@ -305,9 +305,9 @@ int moe_pack_expert_weights(const int8_t *w, moe_proj_t proj, int32_t E, int32_t
  *   ret[slot_offset[p] + i][c] = bf16_rne((f32(acc_d) * hs) * s_down[e][c])
  *   disp_buf   as written by moe_dispatch_q8 (16B)
  *   w_gateup   Wgu = [E][2I][H] int8 (rows 0..I-1 gate, I..2I-1 up) in the tile image of
- *              moe_pack_expert_weights (MOE_PROJ_GATEUP), 16B;  s_gateup [E][2I] fp32
+ *              moe_pack_expert_weights (MOE_PROJ_GATEUP), 16B;  s_gateup [E][2I] fp32, 16B
  *   w_down     Wd = [E][H][I] int8 in the tile image of moe_pack_expert_weights
- *              (MOE_PROJ_DOWN), 16B;  s_down [E][H] fp32
+ *              (MOE_PROJ_DOWN), 16B;  s_down [E][H] fp32, 16B
  *   I          multiple of 64, <= 16384 (H a multiple of 128)
  *   ret        [T*k][H] bf16, 16B
  *   acc_gateup_dbg [T*k][2I] int32 or NULL, acc_down_dbg [T*k][H] int32 or NULL:

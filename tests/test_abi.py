@@ -86,6 +86,13 @@ def test_invalid_arguments_rejected_before_launch():
         assert L.moe_expert_ffn_q8(fake, fake, fake, fake, fake, fake, fake, fake, fake, bad_i,
                                    ctypes.byref(g), fake, None, None, fake, 1 << 30,
                                    None) == moe.MOE_ERR_UNSUPPORTED
+    # the expert epilogues read the channel scales four at a time: 16-byte aligned
+    g128 = moe.geom(T=16, H=128, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    odd4 = ctypes.c_void_p(0x1004)
+    assert L.moe_expert_gateup_q8(fake, fake, fake, fake, fake, fake, odd4, 64, ctypes.byref(g128),
+                                  None, fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_down_q8(fake, fake, fake, fake, odd4, 64, ctypes.byref(g128), fake, None,
+                                fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     # relay hop without relays configured
     assert L.moe_relay_returns(fake, fake, fake, fake, ctypes.byref(g), fake,
                                None) == moe.MOE_ERR_INVALID_ARG
