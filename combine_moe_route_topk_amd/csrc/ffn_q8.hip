@@ -19,11 +19,11 @@
 //            return rows.
 // Tiles: 128 x 256 outputs per 256-thread block (four wavefronts of 128 x 64,
 // each 4 x 2 MFMA 32x32 blocks), K steps of 64 bytes.  The A rows move
-// global -> LDS by DMA into a ring of four stages, three steps ahead,
+// global -> LDS by DMA into a ring of four stages, two steps ahead,
 // XOR-swizzled rows.  The weights come pre-packed (moe_pack_expert_weights) in
 // MFMA fragment order: each wavefront loads its own 64 columns of a K step
 // straight into a ring of four register buffers, 4 KB as four contiguous 1 KB
-// runs of whole cache lines, also three steps ahead of the MFMAs.  The work
+// runs of whole cache lines, also two steps ahead of the MFMAs.  The work
 // list is ordered slot-major, then groups of kGroupM m-tiles, then n-tiles,
 // then m inside the group, and blocks are remapped so that each XCD walks one
 // contiguous stretch of it: the m-tiles of a group share every weight tile in
@@ -144,8 +144,8 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 //              epilogue: bf16 return rows.
 // Block tile 128 x 256, four wavefronts side by side along N, each owning all
 // 128 rows x 64 columns (4 x 2 MFMA 32x32 blocks, 128 accumulators): the four
-// waves share every A fragment read from LDS.  The loads of step kt + 3 are in
-// flight while step kt feeds the MFMAs (kt + 2 in ROUTER mode); one barrier
+// waves share every A fragment read from LDS.  The loads of step kt + 2 are in
+// flight while step kt feeds the MFMAs (also in ROUTER mode); one barrier
 // per K step; two blocks per CU overlap each other's waits.
 // Q8OUT (DOWN only): the return rows are INT8 with one fp32 scale per 256
 // columns (the n-tile) instead of bf16 -- see the epilogue.
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       }
     }
   } else {
-    // B straight from the packed image into registers, three K steps ahead, in a
+    // B straight from the packed image into registers, two K steps ahead, in a
     // ring of four register buffers: each wavefront reads only its own 64
     // columns, 4 KB per step as four 1 KB runs in MFMA fragment order (the image
     // holds them so); A keeps the LDS DMA, at the same distance, so one vmcnt per
@@ -343,9 +343,11 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     // its load and the MFMA that reads it, and no load may be in flight when the
     // loop ends -- which the library's build checks on the assembly.  The steps
     // are padded to a whole number of groups of four (zero weights in the
-    // image), the loop issues its loads unconditionally, and the last three
-    // steps issue none and wait statically (12, 6, 0 loads in flight).
-    constexpr int kDepth = 3, kAStages = 4;
+    // image), the loop issues its loads unconditionally, and the last two
+    // steps issue none and wait statically (6, then 0 loads in flight).  Two
+    // steps ahead measured faster than three (2-3%; one step ahead is slower):
+    // more loads in flight only queue longer.
+    constexpr int kDepth = 2, kAStages = 4;
     static_assert(kAStages * BM * LDS_STRIDE <= kStages * (BM + BN) * LDS_STRIDE, "A ring fits");
     const int KTp = (KT + 3) & ~3;
     const uint8_t *bsrc = (const uint8_t *)w + ((int64_t)e * NT + tl.n) * KTp * kPackedStepBytes +
@@ -381,19 +383,16 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    using W12 = std::integral_constant<int, 12>;
     using W6 = std::integral_constant<int, 6>;
     using W0 = std::integral_constant<int, 0>;
     using Yes = std::true_type;
     using No = std::false_type;
     // one K step: buffer B of the ring, W loads of later steps allowed in flight,
-    // ISSUE: start the loads of step kt + 3
+    // ISSUE: start the loads of step kt + 2
     auto step = [&](auto bi, auto wi, auto issue, auto ntw, int kt) __attribute__((always_inline)) {
       constexpr int B = decltype(bi)::value, W = decltype(wi)::value;
-      if constexpr (W == 12)
-        __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12)
-      else if constexpr (W == 6)
-        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+      if constexpr (W == 6)
+        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): the loads of the next step
       else
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __builtin_amdgcn_s_barrier();
@@ -431,16 +430,14 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       dma_a(0, a_stage(0));
       load_b(I1{}, ntw, 1);
       dma_a(min(1, KT - 1), a_stage(1));
-      load_b(I2{}, ntw, 2);
-      dma_a(min(2, KT - 1), a_stage(2));
       for (int kt0 = 0; kt0 < KTp - 4; kt0 += 4) {
-        step(I0{}, W12{}, Yes{}, ntw, kt0);
-        step(I1{}, W12{}, Yes{}, ntw, kt0 + 1);
-        step(I2{}, W12{}, Yes{}, ntw, kt0 + 2);
-        step(I3{}, W12{}, Yes{}, ntw, kt0 + 3);
+        step(I0{}, W6{}, Yes{}, ntw, kt0);
+        step(I1{}, W6{}, Yes{}, ntw, kt0 + 1);
+        step(I2{}, W6{}, Yes{}, ntw, kt0 + 2);
+        step(I3{}, W6{}, Yes{}, ntw, kt0 + 3);
       }
-      step(I0{}, W12{}, Yes{}, ntw, KTp - 4);  // starts the loads of the last step
-      step(I1{}, W12{}, No{}, ntw, KTp - 3);
+      step(I0{}, W6{}, Yes{}, ntw, KTp - 4);
+      step(I1{}, W6{}, Yes{}, ntw, KTp - 3);  // starts the loads of the last step
       step(I2{}, W6{}, No{}, ntw, KTp - 2);
       step(I3{}, W0{}, No{}, ntw, KTp - 1);  // vmcnt(0): nothing is in flight past this point
     };
