@@ -24,7 +24,7 @@
 // MFMA fragment order: each wavefront loads its own 64 columns of a K step
 // straight into a ring of four register buffers, 4 KB as four contiguous 1 KB
 // runs of whole cache lines, also two steps ahead of the MFMAs.  The work
-// list is ordered slot-major, then groups of kGroupM m-tiles, then n-tiles,
+// list is ordered slot-major, then groups of m-tiles (kGroupM), then n-tiles,
 // then m inside the group, and blocks are remapped so that each XCD walks one
 // contiguous stretch of it: the m-tiles of a group share every weight tile in
 // that XCD's L2.  Weight tiles that only one block reads, and the outputs,
@@ -51,7 +51,9 @@ constexpr int LDS_STRIDE = BK;  // bytes per LDS row
 // makes both access patterns conflict-free: the staging stores (16 lanes =
 // four rows x four chunks) and the MFMA operand reads (16 lanes = sixteen rows,
 // one chunk: rows r, r+4, r+8, r+12 would share banks without it).
-constexpr int kGroupM = 8;
+// m-tiles per group: gate/up 4 (its A rows, 7 KB each, are the bigger
+// operand to keep in L2: 1.4% faster than 8 on the Zipf layer), down 8
+template <int MODE> constexpr int kGroupM = MODE == 0 /* GATEUP */ ? 4 : 8;
 // LDS arena: three stages of (A + B) rows -- the gate logits' ring, DMA two K
 // steps ahead; the INT8 projections hold their four A stages in it
 constexpr int kStages = 3;
@@ -95,7 +97,8 @@ struct Tile {
   int p, m, n;
   int gsz;  // m-tiles in this tile's group: the blocks that read the same weight n-tile
 };
-// Returns false when this block has no work.
+// Returns false when this block has no work.  GM: m-tiles per group.
+template <int GM>
 __device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t *slot_count,
                                             int P, int NT, Tile &tl) {
   const int64_t total = (int64_t)tiles[P] * NT;
@@ -115,13 +118,13 @@ __device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t 
   const int p = lo;
   const int mt = (slot_count[p] + BM - 1) / BM;
   const int64_t local = L - (int64_t)tiles[p] * NT;
-  const int g = (int)(local / ((int64_t)kGroupM * NT));
-  const int rem = (int)(local % ((int64_t)kGroupM * NT));
-  const int gsz = min(kGroupM, mt - g * kGroupM);
+  const int g = (int)(local / ((int64_t)GM * NT));
+  const int rem = (int)(local % ((int64_t)GM * NT));
+  const int gsz = min(GM, mt - g * GM);
   tl.p = p;
   tl.gsz = gsz;
   tl.n = rem / gsz;
-  tl.m = g * kGroupM + rem % gsz;
+  tl.m = g * GM + rem % gsz;
   return true;
 }
 
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     row0 = (int64_t)tl.m * BM;
     rows_here = (int)min((int64_t)BM, nrows - row0);
   } else {
-    if (!decode_tile(tiles, slot_count, P, NT, tl)) return;
+    if (!decode_tile<kGroupM<MODE>>(tiles, slot_count, P, NT, tl)) return;
     e = slot_logical[tl.p];
     if (e < 0 || e >= E) return;
     const int cnt = slot_count[tl.p];
