@@ -27,14 +27,15 @@ MOE_DEVICE_OVER_CAPACITY = 4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATING_SOFTMAX, GATING_SIGMOID = 0, 1
-RET_Q8_FROM_DISPATCH, RET_BF16, RET_Q8_BLOCKS = 0, 1, 2
+RET_Q8_FROM_DISPATCH, RET_BF16, RET_Q8_BLOCKS, RET_Q8_ROWS = 0, 1, 2, 3
 RET_Q8_BLOCK = 256  # columns per scale of the INT8 expert returns
 PROJ_GATEUP, PROJ_DOWN = 0, 1
 
 EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispatch_q8",
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
-            "moe_pack_expert_weights", "moe_router_topk", "moe_status_string")
+            "moe_pack_expert_weights", "moe_router_topk", "moe_quant_returns_q8",
+            "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -96,6 +97,7 @@ def lib():
                                       _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
+        L.moe_quant_returns_q8.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -249,6 +251,11 @@ def moe_relay_returns(ret, phys_ids, slot_partition, ret_row, g: Geom, comb_row,
     _check(lib().moe_relay_returns(_ptr(ret), _ptr(phys_ids), _ptr(slot_partition), _ptr(ret_row),
                                    ctypes.byref(g), _ptr(comb_row), _stream(stream)),
            "moe_relay_returns")
+
+
+def moe_quant_returns_q8(ret, slot_offset, g: Geom, ret_q8, stream=None):
+    _check(lib().moe_quant_returns_q8(_ptr(ret), _ptr(slot_offset), ctypes.byref(g), _ptr(ret_q8),
+                                      _stream(stream)), "moe_quant_returns_q8")
 
 
 def moe_combine(mode: int, src, row, topk_w, g: Geom, out_dtype: int, out, stream=None):

@@ -132,14 +132,19 @@ extern "C" int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *
   int st = validate_geom(g);
   if (st != MOE_OK) return st;
   if (g->T > 0 && (!src || !row || !topk_w || !out)) return MOE_ERR_INVALID_ARG;
-  if (mode != MOE_RET_Q8_FROM_DISPATCH && mode != MOE_RET_BF16 && mode != MOE_RET_Q8_BLOCKS)
+  if (mode != MOE_RET_Q8_FROM_DISPATCH && mode != MOE_RET_BF16 && mode != MOE_RET_Q8_BLOCKS &&
+      mode != MOE_RET_Q8_ROWS)
     return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if (g->T == 0) return MOE_OK;
+  // Q8_ROWS: token-wise INT8 returns, the message layout (codes, then the row's
+  // scale at byte H) at the INT8 return row size
   const bool qb = mode == MOE_RET_Q8_BLOCKS;
-  const bool q8 = mode == MOE_RET_Q8_FROM_DISPATCH || qb;
-  const int64_t rb = qb ? ret_q8_row_bytes_of(*g) : q8 ? msg_bytes_of(*g) : (int64_t)g->H * 2;
+  const bool q8 = mode == MOE_RET_Q8_FROM_DISPATCH || mode == MOE_RET_Q8_ROWS || qb;
+  const int64_t rb = (qb || mode == MOE_RET_Q8_ROWS) ? ret_q8_row_bytes_of(*g)
+                     : q8                           ? msg_bytes_of(*g)
+                                                    : (int64_t)g->H * 2;
   const dim3 grid((unsigned)((g->T + 3) / 4));
   hipStream_t s = (hipStream_t)stream;
   const bool obf = out_dtype == MOE_DTYPE_BF16;
@@ -152,6 +157,107 @@ extern "C" int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *
     launch_combine<8>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
   else
     launch_combine<16>(q8, qb, obf, grid, s, sp, row, topk_w, *g, rb, out);
+  return launch_status();
+}
+
+// ------------------------------------------------ token-wise INT8 returns ---
+namespace moe {
+namespace {
+// One wavefront per dense return row (the send side of the return path): the
+// row's bf16 values are loaded once into registers (lane l holds the 16-byte
+// chunks i * 64 + l, eight values each), amax by a wavefront max, s = amax / 127
+// (IEEE divide), then every value's code; each lane stores the eight codes of a
+// chunk as one 8-byte store (512 consecutive bytes per wave instruction) and
+// lane 0 the scale at byte H.  The quotient y / s is taken with the row's
+// reciprocal r = 1 / s and one Markstein correction, q0 = y r,
+// q = fma(fma(-q0, s, y), r, q0), which gives the IEEE quotient's code for
+// every pair of bf16 values |y| <= amax when s >= 2^-100 (checked for all such
+// pairs on the host); below that the division itself is used.
+template <int NIT>
+__global__ __launch_bounds__(256) void quant_returns_kernel(const uint16_t *__restrict__ ret,
+                                                            const int32_t *__restrict__ slot_offset,
+                                                            int P, int H, int64_t nrows,
+                                                            int64_t row_bytes,
+                                                            uint8_t *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= nrows || r >= slot_offset[P]) return;
+  const int nch = H / 8;  // 16-byte chunks of the bf16 row
+  const uint16_t *src = ret + r * H;
+  uint4 v[NIT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int c = i * 64 + lane;
+    if (c < nch) {
+      const v4u lv = __builtin_nontemporal_load((const v4u *)(src + 8 * c));
+      v[i] = make_uint4(lv.x, lv.y, lv.z, lv.w);
+      const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(wd[q] & 0xffffu)),
+                                 fabsf(bf16_bits_to_f32(wd[q] >> 16))));
+    }
+  }
+  amax = wave_max_f32(amax);
+  const float s = amax / 127.0f;
+  const float rs = s >= 0x1p-100f ? 1.0f / s : 0.0f;  // 0: divide
+  uint8_t *dst = out + r * row_bytes;
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int c = i * 64 + lane;
+    if (c >= nch) break;
+    const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    // code + 128 = median(rint(q) + 128, 1, 255), converted into its byte of the
+    // packed word; the xor with 0x80 per byte turns it back into the int8 code
+    uint32_t pk[2] = {0x80808080u, 0x80808080u};  // code 0 (s = 0)
+    auto put = [&](int e, float q) __attribute__((always_inline)) {
+      const float t = __builtin_amdgcn_fmed3f(rintf(q) + 128.0f, 1.0f, 255.0f);
+      pk[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(t, e & 3, pk[e >> 2]);
+    };
+    auto y_of = [&](int e) __attribute__((always_inline)) {
+      return bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    };
+    if (s != 0.0f && rs != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = y_of(e), q0 = y * rs;
+        put(e, fmaf(fmaf(-q0, s, y), rs, q0));
+      }
+    } else if (s != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) put(e, y_of(e) / s);
+    }
+    *(uint2 *)(dst + 8 * c) = make_uint2(pk[0] ^ 0x80808080u, pk[1] ^ 0x80808080u);
+  }
+  if (lane == 0) *(float *)(dst + H) = s;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_quant_returns_q8(const uint16_t *ret, const int32_t *slot_offset,
+                                    const moe_geom_t *g, void *ret_q8, void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (g->relays > 0) return MOE_ERR_UNSUPPORTED;  // the E2A hop moves bf16 rows
+  const int64_t n = (int64_t)g->T * g->k;
+  if (n == 0) return MOE_OK;
+  if (!ret || !slot_offset || !ret_q8) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ret) || !aligned16(ret_q8)) return MOE_ERR_INVALID_ARG;
+  const int nit = (g->H / 8 + 63) / 64;
+  const dim3 grid((unsigned)((n + 3) / 4));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rb = ret_q8_row_bytes_of(*g);
+  uint8_t *o = (uint8_t *)ret_q8;
+#define MOE_QR(N)                                                                              \
+  hipLaunchKernelGGL((quant_returns_kernel<N>), grid, dim3(256), 0, s, ret, slot_offset, g->P, \
+                     g->H, n, rb, o)
+  if (nit <= 2) MOE_QR(2);
+  else if (nit <= 4) MOE_QR(4);
+  else if (nit <= 8) MOE_QR(8);
+  else if (nit <= 16) MOE_QR(16);
+  else MOE_QR(32);
+#undef MOE_QR
   return launch_status();
 }
 

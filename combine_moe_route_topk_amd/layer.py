@@ -14,9 +14,10 @@ from typing import Optional
 import torch
 
 from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, PROJ_DOWN, PROJ_GATEUP,
-               RET_BF16, RET_Q8_BLOCKS, RET_Q8_FROM_DISPATCH, Geom, geom, moe_combine,
+               RET_BF16, RET_Q8_BLOCKS, RET_Q8_FROM_DISPATCH, RET_Q8_ROWS, Geom, geom, moe_combine,
                moe_dispatch_q8, moe_expert_down_q8, moe_expert_down_q8_int8ret, moe_expert_ffn_q8,
-               moe_expert_gateup_q8, moe_pack_expert_weights, moe_plan_sizes, moe_relay_returns,
+               moe_expert_gateup_q8, moe_pack_expert_weights, moe_plan_sizes, moe_quant_returns_q8,
+               moe_relay_returns,
                moe_route_topk, moe_router_logits, moe_router_topk)
 
 
@@ -240,15 +241,24 @@ class MoeLayer:
         moe_expert_down_q8_int8ret(b.slot_count, b.slot_offset, self.slot_logical, wd, sd, self.I,
                                    self.g, b.ret_q8_rows(), acc_down_dbg, b.fscratch)
 
+    def quant_returns(self):
+        """Token-wise INT8 of the bf16 return rows (one scale per row), into the INT8
+        return rows that combine('q8rows') reads."""
+        b = self.buf
+        moe_quant_returns_q8(b.ret, b.slot_offset, self.g, b.ret_q8_rows())
+
     def combine(self, mode: str):
-        """mode 'q8' (identity experts: dispatched messages), 'bf16' (bf16 returns) or
-        'q8blocks' (INT8 returns of experts_down_int8ret)."""
+        """mode 'q8' (identity experts: dispatched messages), 'bf16' (bf16 returns),
+        'q8blocks' (INT8 returns of experts_down_int8ret) or 'q8rows' (token-wise INT8
+        returns of quant_returns)."""
         b = self.buf
         odt = DTYPE_BF16 if self.out_dtype == torch.bfloat16 else DTYPE_F32
         if mode == "q8":
             moe_combine(RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, b.topk_w, self.g, odt, b.out)
         elif mode == "q8blocks":
             moe_combine(RET_Q8_BLOCKS, b.ret_q8_rows(), b.ret_row, b.topk_w, self.g, odt, b.out)
+        elif mode == "q8rows":
+            moe_combine(RET_Q8_ROWS, b.ret_q8_rows(), b.ret_row, b.topk_w, self.g, odt, b.out)
         else:
             row = b.ret_row
             if self.g.relays:
@@ -258,7 +268,8 @@ class MoeLayer:
 
     def forward(self, x, logits, combine: str = "bf16"):
         """route -> dispatch -> experts -> combine; combine 'q8blocks' runs the experts
-        with INT8 return rows."""
+        with INT8 return rows (block scales), 'q8rows' quantizes the bf16 returns
+        token-wise before the combine."""
         self.route(logits)
         self.dispatch(x)
         if self.weights is not None:
@@ -267,6 +278,8 @@ class MoeLayer:
                 self.experts_down_int8ret()
             else:
                 self.experts()
+                if combine == "q8rows":
+                    self.quant_returns()
         self.combine(combine)
         return self.buf.out
 

@@ -80,8 +80,11 @@ typedef enum { MOE_PROJ_GATEUP = 0, MOE_PROJ_DOWN = 1 } moe_proj_t;
 typedef enum {
   MOE_RET_Q8_FROM_DISPATCH = 0, /* value rows are dispatch messages (int8 + scale) */
   MOE_RET_BF16 = 1,             /* value rows are bf16 expert returns              */
-  MOE_RET_Q8_BLOCKS = 2         /* value rows are INT8 expert returns: H codes and */
+  MOE_RET_Q8_BLOCKS = 2,        /* value rows are INT8 expert returns: H codes and */
                                 /* one fp32 scale per MOE_RET_Q8_BLOCK columns     */
+  MOE_RET_Q8_ROWS = 3           /* value rows are token-wise INT8 expert returns   */
+                                /* (moe_quant_returns_q8): H codes, then one fp32  */
+                                /* scale for the whole row at byte H               */
 } moe_ret_mode_t;
 
 /* Columns per scale of the INT8 expert returns (the down projection's n-tile). */
@@ -367,6 +370,28 @@ int moe_expert_down_q8_int8ret(const int32_t *slot_count, const int32_t *slot_of
                                void *stream);
 
 /*
+ * moe_quant_returns_q8 -- token-wise INT8 expert returns [XDS DeepSeek INT8 量化:
+ * P085 gives activations one scale per token, P089 quantizes the expert outputs
+ * to INT8 before they travel back, the quantization fused into that transfer].
+ * Each dense bf16 return row y (as written by moe_expert_down_q8) gets the
+ * token rule of moe_dispatch_q8 over the whole row:
+ *   s = max_c |y[c]| / 127 (fp32),  q[c] = clamp(round_half_even(y[c] / s), +-127)
+ *   (fp32 quotients; an all-zero row gives s = 0 and q = 0).
+ * This is the send side of the return path: it reads each return row once and
+ * writes the row that travels, half the bytes of the bf16 row.
+ *   ret         [T*k][H] bf16, 16B (rows [0, slot_offset[P]) are converted)
+ *   slot_offset [P+1] as written by moe_dispatch_q8 (read on the device)
+ *   ret_q8      [T*k][ret_q8_row_bytes] (moe_plan_sizes), 16B: row i holds the H
+ *               codes, then the fp32 scale at byte H; the bytes after it are
+ *               left as they were
+ * Combine these rows with mode MOE_RET_Q8_ROWS.  Geometries with relays are not
+ * supported (MOE_ERR_UNSUPPORTED): the E2A hop moves bf16 rows.
+ * Errors: MOE_ERR_INVALID_ARG (NULL or misaligned pointers), MOE_ERR_UNSUPPORTED.
+ */
+int moe_quant_returns_q8(const uint16_t *ret, const int32_t *slot_offset, const moe_geom_t *g,
+                         void *ret_q8, void *stream);
+
+/*
  * moe_relay_returns -- E2A second hop of the two-hop trampoline [XDS 解耦 A2A,
  * P045, Fig. 8: E2A runs the A2E path in reverse].  With g->relays = R > 0, the
  * return row of every route whose slot lives on a partition d >= R is copied
@@ -389,6 +414,8 @@ int moe_relay_returns(uint16_t *ret, const int32_t *phys_ids, const int32_t *slo
  *   mode BF16:             src = ret [rows][H] bf16, row = ret_row (or comb_row)
  *   mode Q8_BLOCKS:        src = ret_q8 (moe_expert_down_q8_int8ret), row = ret_row;
  *                          v = f32(q[c]) * scale[c / 256] [XDS DeepSeek INT8 量化, P089]
+ *   mode Q8_ROWS:          src = ret_q8 (moe_quant_returns_q8), row = ret_row;
+ *                          v = f32(q[c]) * scale (one per row) [XDS P085, P089]
  *   topk_w  [T][k] fp32;  out [T][H] fp32 or bf16 (out_dtype, RNE), 16B.
  *   Routes with row < 0 contribute nothing.
  */

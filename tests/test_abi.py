@@ -117,7 +117,13 @@ def test_int8_returns_and_router_validation():
     assert L.moe_expert_down_q8_int8ret(None, fake, fake, fake, fake, 256, ctypes.byref(g), fake,
                                         None, fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     # combine: an unknown return mode
-    assert L.moe_combine(3, fake, fake, fake, ctypes.byref(g), 0, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(4, fake, fake, fake, ctypes.byref(g), 0, fake, None) == moe.MOE_ERR_INVALID_ARG
+    # token-wise INT8 returns: not with relays, NULL and misaligned pointers refused
+    assert L.moe_quant_returns_q8(fake, fake, ctypes.byref(relay), fake,
+                                  None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_returns_q8(None, fake, ctypes.byref(g), fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_returns_q8(fake, fake, ctypes.byref(g), ctypes.c_void_p(0x1004),
+                                  None) == moe.MOE_ERR_INVALID_ARG
     # router: H a multiple of 32, E a multiple of 4, scratch large enough, 16-byte alignment
     odd_h = moe.geom(T=16, H=80, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
     assert L.moe_router_logits(fake, fake, ctypes.byref(odd_h), fake, fake, 1 << 30,

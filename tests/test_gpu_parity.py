@@ -413,14 +413,50 @@ def test_dispatch_twohop_small_equals_direct():
                           gather_rows(direct.layer.buf, rows)[:, :n])
 
 
-def test_dispatch_twohop46080_full_layout_sampled_rows():
-    """46080 tokens from 160 sources to 288 partitions through 160 relays:
-    full layout, and the message rows of four token ranges (first, last, two inner)."""
+def test_dispatch_twohop46080_full_layout_all_rows():
+    """46080 tokens from 160 sources to 288 partitions through 160 relays: full
+    layout, and every one of the 368,640 message rows (checked in token chunks)."""
     c = Case(mw.WORKLOADS["twohop46080"])
     _, _, phys = _check_route(c)
     T = c.w.T
-    _check_dispatch(c, phys, row_sample=[(0, 512), (T // 3, T // 3 + 512), (T // 2 + 7, T // 2 + 300),
-                                         (T - 512, T)])
+    _check_dispatch(c, phys, row_sample=[(t0, min(T, t0 + 2048)) for t0 in range(0, T, 2048)])
+
+
+def test_twohop46080_e2a_combine_full_size():
+    """The E2A hop and the combine at full size (46080 tokens, 288 partitions, 160
+    relays; the routes to partitions >= 160 come back through relay staging):
+    synthetic bf16 returns for all 368,640 routes; 1024 sampled tokens compared
+    with the oracle's combine of the same returns, bit for bit given the same
+    fp32 weights and within the bf16 tolerance end to end (oracle weights)."""
+    w = mw.WORKLOADS["twohop46080"]
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    c.layer.dispatch(c.x_d)
+    b = c.layer.buf
+    torch.cuda.synchronize()
+    rr = host(b.ret_row).ravel()
+    n = w.T * w.k
+    assert np.array_equal(np.sort(rr), np.arange(n)), "every route has its own return row"
+    for r0 in range(0, n, 32768):
+        routes = np.arange(r0, min(n, r0 + 32768))
+        vals = torch.from_numpy(mw.route_returns(w, routes).view(np.int16)).cuda()
+        b.ret[:n].index_copy_(0, torch.from_numpy(rr[routes].astype(np.int64)).cuda(), vals)
+        del vals
+    c.layer.combine("bf16")
+    torch.cuda.synchronize()
+    comb = host(b.comb_row)
+    assert int((comb >= n).sum()) > 0.3 * n, "routes to partitions >= 160 go through the relays"
+    out = host(b.out.view(torch.int16)).view(np.uint16)
+    rng = np.random.default_rng(5)
+    tsel = np.sort(rng.choice(w.T, 1024, replace=False))
+    routes = (tsel[:, None] * w.k + np.arange(w.k)).ravel()
+    vals = mw.route_returns(w, routes)
+    ident = np.arange(len(routes), dtype=np.int32).reshape(len(tsel), w.k)
+    w_gpu = host(b.topk_w)[tsel]
+    ref = oracle.combine(vals, ident, w_gpu, w.k, w.H, "bf16", True)
+    assert np.array_equal(out[tsel], ref), "E2A + combine bits (same fp32 weights)"
+    ref2 = oracle.combine(vals, ident, tw[tsel].astype(np.float32), w.k, w.H, "bf16", True)
+    assert_close(bf16_to_f32(out[tsel]), bf16_to_f32(ref2), BF16_RTOL, BF16_ATOL, "end to end")
 
 
 def test_dispatch_is_deterministic():
@@ -625,12 +661,96 @@ def test_layer_int8_returns_small_end_to_end():
     assert_close(bf16_to_f32(out), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL, "layer output")
 
 
+def _tokenwise_return_rows_oracle(w, y_rows, rb):
+    """The token rule over the whole bf16 return row (one scale per row)."""
+    q, s = oracle.quant_blocks(y_rows, w.H)
+    return oracle.int8_return_rows(q, s, rb)
+
+
+def test_expert_int8_tokenwise_returns_and_combine_small():
+    """Token-wise INT8 expert returns (XDS P085's one scale per token applied to
+    P089's quantized outputs): every row bit-exact (H codes and the row scale)
+    against the oracle's token rule on its bf16 returns, and the combine of those
+    rows bit-exact against the oracle's combine of the same rows (fp32 and bf16)."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
+    b = c.layer.buf
+    rb = b.sizes.ret_q8_row_bytes
+    c.layer.experts()
+    c.layer.quant_returns()
+    torch.cuda.synchronize()
+    got = host(b.ret_q8_rows())
+    logical = c.sl[phys.ravel()]
+    rr = lay["ret_row"].ravel()
+    for e in np.unique(logical):
+        sel = np.nonzero(logical == e)[0]
+        toks = sel // w.k
+        y, *_ = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e])
+        exp = _tokenwise_return_rows_oracle(w, y, rb)
+        assert np.array_equal(got[rr[sel], :w.H + 4], exp[:, :w.H + 4]), f"rows, expert {e}"
+    w32 = host(b.topk_w)
+    for odt, obf in ((torch.float32, False), (torch.bfloat16, True)):
+        c.layer.out_dtype = odt
+        b.out = torch.empty((w.T, w.H), dtype=odt, device="cuda")
+        c.layer.combine("q8rows")
+        torch.cuda.synchronize()
+        ref = oracle.combine(got, lay["ret_row"], w32, w.k, w.H, "q8", obf, scale_offset=w.H)
+        out = host(b.out.view(torch.int16)).view(np.uint16) if obf else host(b.out)
+        assert np.array_equal(out, ref), f"combine of token-wise INT8 returns ({odt})"
+
+
+def test_quant_returns_edge_rows():
+    """The token rule on hand-made bf16 return rows, bit-exact: an all-zero row
+    (s = 0, q = 0), a row of one value repeated, exact halves at s = 1 (round half
+    to even), signed zeros, subnormal rows (s below 2^-100: the division path),
+    values near the bf16 maximum, and a ragged tail of rows (T*k = 7 rows)."""
+    H = 1024
+    g = moe.geom(T=7, H=H, E=1, P=1, k=1, D=1, Epp=1, S=1, LB=7)
+    rng = np.random.default_rng(41)
+    yf = rng.standard_normal((7, H)).astype(np.float32)
+    yf[0] = 0.0
+    yf[1] = -3.25
+    yf[2] = 0.5 + rng.integers(-127, 127, H).astype(np.float32)
+    yf[2, :3] = [127.0, 2.5, -2.5]
+    yf[3] = np.where(rng.random(H) < 0.5, np.float32(-0.0), yf[3] * np.float32(1e-30))
+    yf[4] = rng.integers(-3, 4, H).astype(np.float32) * np.float32(2.0 ** -130)
+    yf[5] = rng.uniform(-3e38, 3e38, H).astype(np.float32)
+    y = mw.to_bf16_bits(yf)
+    sz = moe.moe_plan_sizes(g, 0)
+    rb = sz.ret_q8_row_bytes
+    out = torch.full((7, rb), 0x5A, dtype=torch.uint8, device="cuda")
+    moe.moe_quant_returns_q8(to_dev(y.view(np.int16)), to_dev(np.array([0, 7], np.int32)), g, out)
+    torch.cuda.synchronize()
+    got = host(out)
+    q, sc = oracle.quant_blocks(y, H)
+    exp = oracle.int8_return_rows(q, sc, rb)
+    assert np.array_equal(got[:, :H + 4], exp[:, :H + 4])
+    assert np.all(got[:, H + 4:] == 0x5A), "bytes after the scale are left as they were"
+    assert sc[0, 0] == 0 and np.all(q[0] == 0) and sc[2, 0] == 1 and q[2, :3].tolist() == [127, 2, -2]
+
+
+def test_layer_int8_tokenwise_returns_small_end_to_end():
+    """route -> dispatch -> experts -> token-wise INT8 returns -> combine, against
+    the oracle's whole path (its bf16 returns quantized per row, combined in the
+    INT8 mode), within the bf16 tolerance."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), weights = _ffn_case(w)
+    out = host(c.layer.forward(c.x_d, c.lg_d, combine="q8rows").view(torch.int16)).view(np.uint16)
+    r = oracle.moe_layer(w, c.x, c.lg, c.bias, None, None, c.sp, c.sl, event_id=1, weights=weights)
+    rb = c.layer.buf.sizes.ret_q8_row_bytes
+    rows = _tokenwise_return_rows_oracle(w, r["route_returns"], rb)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    ref = oracle.combine(rows, ident, r["topk_w32"], w.k, w.H, "q8", True, scale_offset=w.H)
+    assert_close(bf16_to_f32(out), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL, "layer output")
+
+
 @pytest.mark.parametrize("name,n_micro", [("ffn_small", 2), ("ragged", 3)])
 def test_microbatch_pipeline_equals_one_batch(name, n_micro):
     """The microbatch pipeline (one microbatch per source partition group, each
     on its own stream) gives the single-batch layer's output bit for bit, twice
-    in a row; ffn_small runs the INT8 SwiGLU experts, ragged identity experts
-    with the INT8 combine."""
+    in a row, and matches the oracle's whole layer within the output tolerance;
+    ffn_small runs the INT8 SwiGLU experts, ragged identity experts with the
+    INT8 combine."""
     w = FFN_SMALL if name == "ffn_small" else RAGGED
     if w.experts == "swiglu":
         c, _, _, weights = _ffn_case(w)
@@ -642,17 +762,27 @@ def test_microbatch_pipeline_equals_one_batch(name, n_micro):
     pipe = moe.MoePipeline(c.g, n_micro, w.gating, to_dev(c.sp), to_dev(c.sl), None, None,
                            None if c.bias is None else to_dev(c.bias), c.layer.weights, w.I,
                            c.layer.out_dtype)
+    r = oracle.moe_layer(w, c.x, c.lg, c.bias, None, None, c.sp, c.sl, event_id=1,
+                         weights=weights if w.experts == "swiglu" else None)
     for _ in range(2):
         out = pipe.forward(c.x_d, c.lg_d, combine=mode)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
                            ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
+        # against the oracle's whole layer (its own routing weights)
+        if out.dtype == torch.bfloat16:
+            got = bf16_to_f32(host(out.view(torch.int16)).view(np.uint16))
+            assert_close(got, bf16_to_f32(r["out"]), BF16_RTOL, BF16_ATOL, "pipeline vs oracle")
+        else:
+            assert_close(host(out), r["out"], FP32_RTOL, FP32_ATOL, "pipeline vs oracle")
 
 
 def test_expert_ffn_layer12288_sampled_rows():
     """The headline layer (T=12288, 256 experts, I=2048, Zipf routing), launched as
-    the bench launches it; the oracle recomputes 32 rows of each of four slots
-    (the hottest, the least loaded non-empty and two random ones)."""
+    the bench launches it: the oracle recomputes 32 rows of each of four slots
+    (the hottest, the least loaded non-empty and two random ones) bit for bit, with
+    their INT8 returns in both granularities; the whole layer output equals the
+    oracle's combine of the GPU's return rows; 64 sampled tokens end to end."""
     w = mw.WORKLOADS["layer12288"]
     c = Case(w)
     ids, tw, phys = _check_route(c)
@@ -672,10 +802,22 @@ def test_expert_ffn_layer12288_sampled_rows():
     rng = np.random.default_rng(0)
     slots = {int(np.argmax(sc)), int(nz[np.argmin(sc[nz])])} | set(rng.choice(nz, 2).tolist())
     inv = np.argsort(lay["ret_row"].ravel())  # ret row -> route index
+    # the layer output: the combine of the GPU's own return rows, every token,
+    # bit for bit against the oracle's combine of the same rows and weights
+    c.layer.combine("bf16")
+    torch.cuda.synchronize()
+    out = host(b.out.view(torch.int16)).view(np.uint16)
+    w_gpu = host(b.topk_w)
+    ref_all = oracle.combine(ret, lay["ret_row"], w_gpu, w.k, w.H, "bf16", True)
+    assert np.array_equal(out, ref_all), "combine of the GPU returns, all 12288 tokens"
+    # token-wise INT8 returns of the same rows
+    c.layer.quant_returns()
+    torch.cuda.synchronize()
+    q8r = host(b.ret_q8_rows()).copy()
+    rb = b.sizes.ret_q8_row_bytes
     c.layer.experts_down_int8ret()  # INT8 returns from the same h (scratch still holds it)
     torch.cuda.synchronize()
     q8 = host(b.ret_q8_rows())
-    rb = b.sizes.ret_q8_row_bytes
     nb = w.H + 4 * (w.H // moe.RET_Q8_BLOCK)
     for p in sorted(slots):
         o = lay["slot_offset"][p]
@@ -689,6 +831,21 @@ def test_expert_ffn_layer12288_sampled_rows():
         assert np.array_equal(ret[rows], y), f"slot {p} (expert {e}, {sc[p]} rows)"
         exp = _int8_return_rows_oracle(w, y, rb)
         assert np.array_equal(q8[rows, :nb], exp[:, :nb]), f"INT8 returns, slot {p}"
+        expr = _tokenwise_return_rows_oracle(w, y, rb)
+        assert np.array_equal(q8r[rows, :w.H + 4], expr[:, :w.H + 4]), f"token-wise rows, slot {p}"
+    # end to end on 64 sampled tokens: the oracle recomputes all k expert rows of
+    # each (its own routes, quantization and FFN) and combines with its weights
+    tsel = np.sort(rng.choice(w.T, 64, replace=False))
+    logical = c.sl[phys]
+    vals = np.empty((len(tsel) * w.k, w.H), np.uint16)
+    for e in np.unique(logical[tsel]):
+        ii, jj = np.nonzero(logical[tsel] == e)
+        y, *_ = oracle.expert_ffn(q[tsel[ii]], s[tsel[ii]], wgu[e], sgu[e], wd[e], sd[e])
+        vals[ii * w.k + jj] = y
+    ident = np.arange(len(tsel) * w.k, dtype=np.int32).reshape(len(tsel), w.k)
+    ref = oracle.combine(vals, ident, tw[tsel].astype(np.float32), w.k, w.H, "bf16", True)
+    assert_close(bf16_to_f32(out[tsel]), bf16_to_f32(ref), BF16_RTOL, BF16_ATOL,
+                 "layer output end to end, 64 tokens")
 
 
 # ------------------------------------------------------------ edge cases ---

@@ -458,6 +458,31 @@ def test_quant_blocks_equal_token_rule_per_block():
         assert np.all(np.abs(q[np.arange(n)[live], c0 + i[live]]) == 127)
 
 
+def test_quant_tokenwise_returns_equal_token_rule():
+    """Token-wise INT8 expert returns (XDS P085's one scale per token applied to the
+    outputs P089 quantizes): the row mode (one block spanning the row) gives exactly
+    the codes and scale of the pinned token rule (c3) on the bf16 row, for normal,
+    all-zero, subnormal, huge and exactly-half rows; the row amax maps to +-127."""
+    rng = np.random.default_rng(24)
+    n, H = 12, 384
+    yf = rng.standard_normal((n, H)).astype(np.float32) * rng.uniform(1e-3, 1e3, (n, 1)).astype(np.float32)
+    yf[1] = 0.0
+    yf[2] = rng.integers(-3, 4, H).astype(np.float32) * np.float32(2.0 ** -130)
+    yf[3] = rng.uniform(-3e38, 3e38, H).astype(np.float32)
+    yf[4] = 0.5 + rng.integers(-127, 127, H).astype(np.float32)
+    yf[4, :3] = [127.0, 2.5, -2.5]
+    y = mw.to_bf16_bits(yf)
+    q, s = oracle.quant_blocks(y, H)
+    qt, st = oracle.quant_tokens(y, True)
+    assert s.shape == (n, 1)
+    assert np.array_equal(q, qt) and np.array_equal(s[:, 0].view(np.uint32), st.view(np.uint32))
+    assert s[1, 0] == 0 and np.all(q[1] == 0)
+    assert s[4, 0] == 1 and q[4, :3].tolist() == [127, 2, -2]
+    live = s[:, 0] > 0
+    i = np.abs(_bf16_to_f32(y)).argmax(1)
+    assert np.all(np.abs(q[np.arange(n)[live], i[live]]) == 127)
+
+
 def test_combine_block_scales_reduce_to_row_scale_and_closed_form():
     """Combine of INT8 rows with block scales: with one block spanning the row it
     is the pinned single-scale INT8 mode exactly; k = 1, w = 1 gives q * s of
