@@ -101,15 +101,23 @@ def build_layer(w, log_every=64):
     return layer, x, lg
 
 
-def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
-    """Per-stage and per-step times of `steps` whole steps.  With int8_returns the
-    experts return INT8 rows (one scale per 256 columns) and the combine reads them."""
+def time_gpu(layer, x, lg, steps, warmup, returns="bf16", flush=None):
+    """Per-stage and per-step times of `steps` whole steps.  returns: 'bf16' (the
+    workload's expert returns), 'q8blocks' (INT8 returns, one scale per 256
+    columns, quantized in the down projection's epilogue) or 'q8rows' (token-wise
+    INT8 returns: one scale per row, quantized by moe_quant_returns_q8).  With
+    `flush` (a device buffer), the buffer is overwritten before every step, outside
+    the timed stages, so that each step starts with cold caches."""
     import torch
+    down = {"bf16": layer.experts_down, "q8rows": layer.experts_down,
+            "q8blocks": layer.experts_down_int8ret}[returns]
     stages = [("route", lambda: layer.route(lg)),
               ("dispatch", lambda: layer.dispatch(x)),
               ("gateup", layer.experts_gateup),
-              ("down", layer.experts_down_int8ret if int8_returns else layer.experts_down),
-              ("combine", lambda: layer.combine("q8blocks" if int8_returns else "bf16"))]
+              ("down", down)]
+    if returns == "q8rows":
+        stages.append(("quant_returns", layer.quant_returns))
+    stages.append(("combine", lambda: layer.combine(returns)))
     for _ in range(warmup):
         for _, f in stages:
             f()
@@ -120,6 +128,8 @@ def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
     torch.cuda.synchronize()
     start.record()
     for s in range(steps):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
         for (name, f), (a, b) in zip(stages, ev[s]):
             a.record()
             f()
@@ -133,7 +143,8 @@ def time_gpu(layer, x, lg, steps, warmup, int8_returns=False):
     step_ms = sorted(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(steps))
     q = lambda f: step_ms[min(len(step_ms) - 1, int(f * len(step_ms)))]
     dist = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
-    return total_ms / steps, per, dist
+    ms = total_ms / steps if flush is None else sum(step_ms) / steps
+    return ms, per, dist
 
 
 def time_pipeline(layer, x, lg, w, steps, warmup, n_micro=2):
@@ -196,6 +207,171 @@ def time_router(layer, x, w, steps, warmup):
                     "from the logits); fused = moe_router_topk"}
 
 
+def _median_us(fn, reps, warmup=3):
+    """Median device time of fn() in microseconds, one pair of events per call."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return t[len(t) // 2]
+
+
+def _bits(a, bf16=True):
+    import numpy as np
+    import torch
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_uniform(packed, steps, warmup):
+    """The 12288-token layer with uniform routing (N(0,1) logits, no Zipf bias):
+    every expert gets about T*k/E routes, so the expert GEMMs see full tiles; the
+    reference case for their MFMA fraction."""
+    import torch
+    import combine_moe_route_topk_amd as moe
+    import moe_workloads as mw
+    w = mw.WORKLOADS["layer12288"].scaled(name="layer12288_uniform", zipf=False)
+    ro, rs, sp, sl = mw.identity_map(w)
+    layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
+                         torch.from_numpy(sl).cuda(), weights=packed, I=w.I)
+    x, lg = _bits(mw.hidden(w)), _bits(mw.logits(w))
+    ms, per, dist = time_gpu(layer, x, lg, steps, warmup)
+    A = algorithmic(w)
+    gu = A["gateup_ops"] / (per["gateup"] * 1e-3) / 1e12
+    dn = A["down_ops"] / (per["down"] * 1e-3) / 1e12
+    del layer
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in per.items()},
+            "gateup_TOPS": round(gu, 1), "gateup_frac_int8_peak": round(gu / INT8_PEAK_TOPS, 4),
+            "down_TOPS": round(dn, 1), "down_frac_int8_peak": round(dn / INT8_PEAK_TOPS, 4),
+            "note": "N(0,1) logits without the Zipf bias: about 384 routes per expert"}
+
+
+def time_decode96(reps):
+    """Decode-size dispatch and combine latency: 96 tokens of one source to 256
+    partitions of one expert each (identity experts, INT8 combine to fp32)."""
+    import torch
+    import combine_moe_route_topk_amd as moe
+    import moe_workloads as mw
+    w = mw.WORKLOADS["decode96"]
+    ro, rs, sp, sl = mw.identity_map(w)
+    layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
+                         torch.from_numpy(sl).cuda(), out_dtype=torch.float32)
+    x, lg = _bits(mw.hidden(w)), _bits(mw.logits(w))
+    layer.route(lg)
+    route_us = _median_us(lambda: layer.route(lg), reps)
+    disp_us = _median_us(lambda: layer.dispatch(x), reps)
+    comb_us = _median_us(lambda: layer.combine("q8"), reps)
+    T, H, k = w.T, w.H, w.k
+    db = T * H * 2 + T * k * 4 + T * k * (H + 16) + 3 * T * k * 4 + w.D * w.S * 16
+    cb = T * k * (H + 4) + T * k * 8 + T * H * 4
+    del layer
+    torch.cuda.empty_cache()
+    return {"route_us": round(route_us, 2), "dispatch_us": round(disp_us, 2),
+            "combine_us": round(comb_us, 2),
+            "dispatch_plus_combine_us": round(disp_us + comb_us, 2),
+            "bytes": {"dispatch": db, "combine": cb},
+            "frac_hbm_peak": round((db + cb) / ((disp_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "latency-bound (about 6.9 MB per call pair, cache-resident); median of "
+                    f"{reps} launches each"}
+
+
+def time_eplb4096(packed, steps, warmup):
+    """The 4096-token layer with the redundant-expert plan: the calibration batch is
+    routed on the GPU, its per-expert counts (the collect histogram) go to the
+    planner (moe_eplb_build_map, 32 redundant slots on partitions 256-287), and the
+    step runs through the replica map.  The expert FFN is bound by its weight bytes
+    here, so its HBM fraction is the figure to read."""
+    import numpy as np
+    import torch
+    import combine_moe_route_topk_amd as moe
+    import moe_workloads as mw
+    w = mw.WORKLOADS["eplb4096"]
+    bias = torch.from_numpy(mw.zipf_bias(w)).cuda()
+    ro, rs, sp, sl = mw.identity_map(w.scaled(P=w.E, D=w.E))
+    cal = moe.MoeLayer(moe.geom(w.calib_tokens, w.H, w.E, w.E, w.k, w.E, 1, 1, w.calib_tokens),
+                       w.gating, torch.from_numpy(sp).cuda(), torch.from_numpy(sl).cuda(), bias=bias)
+    counts = []
+    for i in range(w.calib_slices):
+        cal.route(_bits(mw.logits(w, i)))
+        counts.append(cal.buf.expert_counts.cpu().numpy().astype(np.int64))
+    del cal
+    primary = np.arange(w.E, dtype=np.int32)
+    free = np.r_[np.zeros(w.E), np.ones(w.P - w.E)].astype(np.int32)
+    ro, rs, sp, sl, _ = moe.moe_eplb_build_map(np.stack(counts), w.P - w.E, w.D, primary, free)
+    layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
+                         torch.from_numpy(sl).cuda(), torch.from_numpy(ro).cuda(),
+                         torch.from_numpy(rs).cuda(), bias=bias, weights=packed, I=w.I)
+    x, lg = _bits(mw.hidden(w)), _bits(mw.logits(w))
+    ms, per, dist = time_gpu(layer, x, lg, steps, warmup)
+    active = int((layer.buf.expert_counts.cpu().numpy() > 0).sum())
+    R = w.T * w.k
+    # FFN bytes the method must move: each routed expert's three INT8 projections
+    # once, the message rows in, the INT8 intermediate (codes + scale) out and
+    # back, the bf16 return rows out
+    wbytes = active * 3 * w.H * w.I
+    ffn_bytes = wbytes + R * (w.H + 16) + 2 * R * (w.I + 4) + R * w.H * 2
+    ffn_ms = per["gateup"] + per["down"]
+    A = algorithmic(w)
+    del layer
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in per.items()},
+            "active_experts": active, "ffn_bytes": ffn_bytes,
+            "ffn_GBps": round(ffn_bytes / (ffn_ms * 1e-3) / 1e9, 1),
+            "ffn_frac_hbm_peak": round(ffn_bytes / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ffn_TOPS": round((A["gateup_ops"] + A["down_ops"]) / (ffn_ms * 1e-3) / 1e12, 1),
+            "note": "replica map planned from four 1024-token calibration slices routed on the "
+                    "GPU; HBM-bound on the routed experts' weights"}
+
+
+def time_twohop46080(reps):
+    """The 46080-token disaggregated shape: 160 sources to 288 partitions, the routes
+    to partitions 160-287 through relays (A2E: dispatch with the second hop; E2A:
+    the relay hop of the returns and the combine).  Synthetic returns."""
+    import numpy as np
+    import torch
+    import combine_moe_route_topk_amd as moe
+    import moe_workloads as mw
+    w = mw.WORKLOADS["twohop46080"]
+    ro, rs, sp, sl = mw.first32_map(w)
+    layer = moe.MoeLayer(moe.geom_of(w), w.gating, torch.from_numpy(sp).cuda(),
+                         torch.from_numpy(sl).cuda(), torch.from_numpy(ro).cuda(),
+                         torch.from_numpy(rs).cuda())
+    x, lg = _bits(mw.hidden(w)), _bits(mw.logits(w))
+    layer.route(lg)
+    layer.buf.ret.zero_()
+    a2e_us = _median_us(lambda: layer.dispatch(x), reps)
+    e2a_us = _median_us(lambda: layer.combine("bf16"), reps)
+    T, H, k = w.T, w.H, w.k
+    R = T * k
+    n_rel = int((sp[layer.buf.phys.cpu().numpy()] >= w.relays).sum())
+    # A2E: read x and the ids, write every message once, the relayed ones twice
+    # (second hop: read + write); E2A: the relayed return rows copied through the
+    # staging (read + write), the combine's gather and its output
+    a2e = T * H * 2 + R * 4 + R * (H + 16) + 2 * n_rel * (H + 16) + 3 * R * 4 + w.D * w.S * 16
+    e2a = 2 * n_rel * H * 2 + R * H * 2 + R * 8 + T * H * 2
+    del layer
+    torch.cuda.empty_cache()
+    return {"a2e_us": round(a2e_us, 1), "e2a_us": round(e2a_us, 1), "relayed_routes": n_rel,
+            "a2e_bytes": a2e, "e2a_bytes": e2a,
+            "a2e_GBps": round(a2e / (a2e_us * 1e-6) / 1e9, 1),
+            "e2a_GBps": round(e2a / (e2a_us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round((a2e + e2a) / ((a2e_us + e2a_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": f"median of {reps} launches each; the pages' A2E 172 us / E2A 193 us are "
+                    "cross-chip figures (context only)"}
+
+
 def attainable(w, reps=5):
     """Attainable rates on this GPU, for context next to the published peaks: a
     plain 1 GiB device copy (HBM) and the vendor library's dense INT8 GEMM
@@ -237,18 +413,40 @@ def attainable(w, reps=5):
     return out
 
 
-def cpu_baseline(w, budget_s=12.0):
+def host_cpu():
+    """The host's CPU model and shape (sockets x cores per socket x threads per core),
+    from lscpu, and the logical CPUs this process may run on."""
+    import subprocess
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return {"model": info.get("Model name", ""), "sockets": info.get("Socket(s)"),
+            "cores_per_socket": info.get("Core(s) per socket"),
+            "threads_per_core": info.get("Thread(s) per core"),
+            "logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(w, budget_s=12.0, threads=None):
     """The oracle, as it stands, on the host cores: route, quantization, dispatch
     layout and messages, and combine over the whole batch; the expert FFN on a
-    seeded sample of routes, scaled by route count."""
+    seeded sample of routes (the hottest expert first), scaled by route count.
+    `threads` OpenMP threads (default: every CPU this process may use); the
+    oracle's results are the same for any thread count."""
     import numpy as np
 
     import moe_workloads as mw
     import oracle
 
-    threads = len(os.sched_getaffinity(0))
-    if os.environ.get("OMP_NUM_THREADS"):
-        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+        if os.environ.get("OMP_NUM_THREADS"):
+            threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
     oracle.set_threads(threads)
     x, lg, bias = mw.hidden(w), mw.logits(w), mw.zipf_bias(w)
     ro, rs, sp, sl = mw.identity_map(w)
@@ -290,17 +488,8 @@ def cpu_baseline(w, budget_s=12.0):
         n *= 2
     t["ffn"] = ffn_s / n_done * w.T * w.k
     total = sum(t.values())
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return {
         "value": w.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "cpu": f"{model}; {os.cpu_count()} logical CPUs visible, {threads} OpenMP threads used",
         "sample": (f"route, quantization, dispatch layout + messages and combine over all "
                    f"{w.T} tokens; expert FFN on {n_done} sampled routes of {len(experts)} "
                    f"experts (hottest first), scaled by route count to {w.T * w.k} routes"),
@@ -351,6 +540,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attainable", action="store_true",
                     help="skip the device-copy and library-GEMM reference rates")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode96, eplb4096, twohop46080 and uniform-routing lines")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline step (for counter runs: every launch of a "
+                         "kernel then has the headline shape)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
@@ -392,6 +586,10 @@ def main():
     for v in stages.values():
         for kk in list(v):
             v[kk] = round(v[kk], 2)
+    for name in ("route", "dispatch", "combine"):
+        stages[name]["frac_hbm_peak"] = round(stages[name]["GBps"] / HBM_PEAK_GBS, 4)
+    for name in ("gateup", "down"):
+        stages[name]["frac_int8_peak"] = round(stages[name]["TOPS"] / INT8_PEAK_TOPS, 4)
     result = {
         "metric": "MoE dispatch+combine GB/s (% of HBM peak) and MoE-layer tokens/s, T=12288 H=7168 k=8",
         "value": round(w.T / (ms * 1e-3), 1),
@@ -419,20 +617,44 @@ def main():
                      "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
     }
-    # the INT8 return path (XDS P089) timed the same way, reported beside the bf16 one
-    ms8, per8, dist8 = time_gpu(layer, x, lg, args.steps, args.warmup, int8_returns=True)
-    log(f"[bench] INT8 returns: {ms8:.3f} ms/step " +
-        " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per8.items()))
-    dc8_bytes = A["dispatch_bytes"] + A["combine_q8_bytes"]
-    dc8_ms = per8["dispatch"] + per8["combine"]
-    result["int8_returns"] = {
-        "tokens_per_s": round(w.T / (ms8 * 1e-3), 1), "ms_per_step": round(ms8, 4),
-        "stages_us": {k: round(v * 1e3, 2) for k, v in per8.items()},
-        "combine_GBps": round(A["combine_q8_bytes"] / (per8["combine"] * 1e-3) / 1e9, 1),
-        "dispatch_combine": {"GBps": round(dc8_bytes / (dc8_ms * 1e-3) / 1e9, 1),
-                             "bytes": dc8_bytes, "us": round(dc8_ms * 1e3, 2)},
-        "note": "expert returns quantized to INT8 in the down projection's epilogue (one "
-                "fp32 scale per 256 columns); not the headline configuration (bf16 returns)"}
+    if args.headline_only:
+        print(json.dumps(result), flush=True)
+        return
+    # the same step with cold caches: 1 GiB written between steps (outside the stages)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    msc, perc, distc = time_gpu(layer, x, lg, max(5, args.steps // 2), args.warmup, flush=flush)
+    del flush
+    dcc_ms = perc["dispatch"] + perc["combine"]
+    result["cold_cache"] = {
+        "ms_per_step": round(msc, 4), "tokens_per_s": round(w.T / (msc * 1e-3), 1),
+        "step_ms": {k: round(v, 4) for k, v in distc.items()},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in perc.items()},
+        "dispatch_combine": {"GBps": round(dc_bytes / (dcc_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(dc_bytes / (dcc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "note": "a 1 GiB buffer is overwritten before every step (outside the timed stages), "
+                "so each step starts with its inputs out of the caches; the headline figures "
+                "above are hot-cache (steps back to back)"}
+    log(f"[bench] cold caches: {msc:.3f} ms/step")
+    # the INT8 return paths (XDS P089), timed the same way, beside the bf16 one
+    for mode, note in (("q8blocks", "expert returns quantized to INT8 in the down "
+                                    "projection's epilogue, one fp32 scale per 256 columns"),
+                       ("q8rows", "token-wise INT8 expert returns: one fp32 scale per row, "
+                                  "quantized by moe_quant_returns_q8 after the down "
+                                  "projection (the send side of the return path)")):
+        ms8, per8, dist8 = time_gpu(layer, x, lg, args.steps, args.warmup, returns=mode)
+        log(f"[bench] INT8 returns ({mode}): {ms8:.3f} ms/step " +
+            " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per8.items()))
+        cb = A["combine_q8_bytes"] if mode == "q8blocks" else \
+            w.T * w.k * (w.H + 4) + w.T * w.k * 8 + w.T * w.H * 2
+        dc8_bytes = A["dispatch_bytes"] + cb
+        dc8_ms = per8["dispatch"] + per8["combine"]
+        result["int8_returns" if mode == "q8blocks" else "int8_returns_tokenwise"] = {
+            "tokens_per_s": round(w.T / (ms8 * 1e-3), 1), "ms_per_step": round(ms8, 4),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in per8.items()},
+            "combine_GBps": round(cb / (per8["combine"] * 1e-3) / 1e9, 1),
+            "dispatch_combine": {"GBps": round(dc8_bytes / (dc8_ms * 1e-3) / 1e9, 1),
+                                 "bytes": dc8_bytes, "us": round(dc8_ms * 1e3, 2)},
+            "note": note + "; not the headline configuration (bf16 returns)"}
     # the microbatch pipeline: two halves of the sources on two streams
     result["microbatch_pipeline"] = time_pipeline(layer, x, lg, w, args.steps, args.warmup)
     log(f"[bench] 2-microbatch pipeline: {result['microbatch_pipeline']['ms_per_step']:.3f} ms/step")
@@ -440,6 +662,27 @@ def main():
     # the headline step starts from the logits, as the workload defines
     result["router"] = time_router(layer, x, w, args.steps, args.warmup)
     log(f"[bench] router logits: {result['router']['us']:.1f} us")
+    packed = layer.weights
+    del layer, x, lg
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        # the other workloads, each on its own (their figures are context, not the headline)
+        cfg = {}
+        cfg["layer12288_uniform"] = time_uniform(packed, args.steps, args.warmup)
+        log(f"[bench] uniform routing: {cfg['layer12288_uniform']['ms_per_step']:.3f} ms/step")
+        cfg["eplb4096"] = time_eplb4096(packed, args.steps, args.warmup)
+        log(f"[bench] eplb4096: {cfg['eplb4096']['ms_per_step']:.3f} ms/step")
+        del packed
+        torch.cuda.empty_cache()
+        cfg["decode96"] = time_decode96(200)
+        log(f"[bench] decode96: dispatch {cfg['decode96']['dispatch_us']} us, "
+            f"combine {cfg['decode96']['combine_us']} us")
+        cfg["twohop46080"] = time_twohop46080(max(5, args.steps // 5))
+        log(f"[bench] twohop46080: A2E {cfg['twohop46080']['a2e_us']} us, "
+            f"E2A {cfg['twohop46080']['e2a_us']} us")
+        result["configs"] = cfg
+    else:
+        del packed
     if not args.no_attainable:
         log("[bench] attainable rates: device copy, library INT8 GEMM")
         att = attainable(w)
@@ -448,8 +691,13 @@ def main():
             result["roofline"]["frac_of_attainable"] = round(gu_tops / att["int8_gemm_TOPS"], 4)
         result["dispatch_combine"]["frac_of_copy"] = round(dc_gbs / att["copy_GBps"], 4)
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        log("[bench] timing the CPU oracle on a bounded sample: all threads, then one")
+        allc = cpu_baseline(w, args.cpu_budget)
+        one = cpu_baseline(w, args.cpu_budget * 0.75, threads=1)
+        allc["modes"] = {f"{allc['cores']}_threads": {k: allc[k] for k in ("value", "seconds")},
+                         "1_thread": {k: one[k] for k in ("value", "seconds", "sample")}}
+        allc["host"] = host_cpu()
+        result["cpu_baseline"] = allc
     print(json.dumps(result), flush=True)
 
 
