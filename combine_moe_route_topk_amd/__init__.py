@@ -21,6 +21,8 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_CAPACITY = -3
 MOE_ERR_HIP = -5
 
+MOE_STATIC_SCRATCH_BYTES = 16 << 20  # the allocation-free dispatch's scratch per GPU
+
 MOE_DEVICE_BAD_ROUTE = 1
 MOE_DEVICE_BAD_PARTITION = 2
 MOE_DEVICE_OVER_CAPACITY = 4
@@ -35,7 +37,7 @@ EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispa
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
             "moe_pack_expert_weights", "moe_router_topk", "moe_quant_returns_q8",
-            "moe_status_string")
+            "moe_dispatch_q8_static", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -98,6 +100,9 @@ def lib():
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_quant_returns_q8.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P]
+        L.moe_dispatch_q8_static.argtypes = [_P, _I32, _P, _P, ctypes.c_uint32,
+                                             ctypes.POINTER(Geom), _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -184,6 +189,20 @@ def moe_dispatch_q8(x, x_dtype: int, phys_ids, slot_partition, event_id: int, g:
                                  _ptr(disp_row), _ptr(ret_row), _ptr(relay_buf), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream)),
            "moe_dispatch_q8")
+
+
+def moe_dispatch_q8_static(x, x_dtype: int, phys_ids, slot_partition, event_id: int, g: Geom,
+                           disp_buf, meta, slot_count, slot_offset, slot_rows, disp_row, ret_row,
+                           relay_buf, status=None, stream=None):
+    """moe_dispatch_q8 without a scratch argument: the library's own per-GPU array
+    serves as scratch (the call allocates nothing); `status` (device int32 or None)
+    receives the call's device status word."""
+    _check(lib().moe_dispatch_q8_static(_ptr(x), x_dtype, _ptr(phys_ids), _ptr(slot_partition),
+                                        event_id & 0xFFFFFFFF, ctypes.byref(g), _ptr(disp_buf),
+                                        _ptr(meta), _ptr(slot_count), _ptr(slot_offset),
+                                        _ptr(slot_rows), _ptr(disp_row), _ptr(ret_row),
+                                        _ptr(relay_buf), _ptr(status), _stream(stream)),
+           "moe_dispatch_q8_static")
 
 
 def moe_expert_ffn_q8(disp_buf, slot_count, slot_offset, slot_rows, slot_logical, w_gateup,

@@ -26,6 +26,8 @@
 //   4. relay    (two-hop only) second hop: relay region rows -> final region.
 // No atomics decide any order: every row index is a deterministic function of
 // the routes, so the layout is bit-identical run to run.
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -406,12 +408,13 @@ void launch_scatter(bool bf16, dim3 grid, hipStream_t st, const void *x, const i
 
 using namespace moe;
 
-extern "C" int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
-                               const int32_t *slot_partition, uint32_t event_id,
-                               const moe_geom_t *g, void *disp_buf, moe_meta_t *meta,
-                               int32_t *slot_count, int32_t *slot_offset, int32_t *slot_rows,
-                               int32_t *disp_row, int32_t *ret_row, void *relay_buf, void *scratch,
-                               size_t scratch_bytes, void *stream) {
+namespace moe {
+namespace {
+int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
+                  const int32_t *slot_partition, uint32_t event_id, const moe_geom_t *g,
+                  void *disp_buf, moe_meta_t *meta, int32_t *slot_count, int32_t *slot_offset,
+                  int32_t *slot_rows, int32_t *disp_row, int32_t *ret_row, void *relay_buf,
+                  void *scratch, size_t scratch_bytes, void *stream) {
   int st = validate_geom(g);
   if (st != MOE_OK) return st;
   if (!slot_partition || !meta || !slot_count || !slot_offset || !scratch) return MOE_ERR_INVALID_ARG;
@@ -481,4 +484,66 @@ extern "C" int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t
     if ((st = launch_status()) != MOE_OK) return st;
   }
   return MOE_OK;
+}
+
+// Copies the device status word of a dispatch into the caller's int32.
+__global__ void copy_status_kernel(const int32_t *__restrict__ src, int32_t *__restrict__ dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
+// The allocation-free variant's scratch: one copy per GPU, held until the
+// process ends.  In host code this name stands for the host-side shadow, not a
+// device address: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_static_scratch[kMaxDevices];
+
+// Device address of the current device's static scratch (looked up on the first
+// call on that device); nullptr on a HIP error.
+void *static_scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_static_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void *q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_static_scratch[dev].store(q, std::memory_order_release);  // same address if two threads race
+  return q;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
+                               const int32_t *slot_partition, uint32_t event_id,
+                               const moe_geom_t *g, void *disp_buf, moe_meta_t *meta,
+                               int32_t *slot_count, int32_t *slot_offset, int32_t *slot_rows,
+                               int32_t *disp_row, int32_t *ret_row, void *relay_buf, void *scratch,
+                               size_t scratch_bytes, void *stream) {
+  return dispatch_impl(x, x_dtype, phys_ids, slot_partition, event_id, g, disp_buf, meta,
+                       slot_count, slot_offset, slot_rows, disp_row, ret_row, relay_buf, scratch,
+                       scratch_bytes, stream);
+}
+
+extern "C" int moe_dispatch_q8_static(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
+                                      const int32_t *slot_partition, uint32_t event_id,
+                                      const moe_geom_t *g, void *disp_buf, moe_meta_t *meta,
+                                      int32_t *slot_count, int32_t *slot_offset,
+                                      int32_t *slot_rows, int32_t *disp_row, int32_t *ret_row,
+                                      void *relay_buf, int32_t *status, void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (dispatch_scratch_layout(*g).total > (int64_t)MOE_STATIC_SCRATCH_BYTES)
+    return MOE_ERR_CAPACITY;
+  void *sp = static_scratch_ptr();
+  if (!sp) return MOE_ERR_HIP;
+  st = dispatch_impl(x, x_dtype, phys_ids, slot_partition, event_id, g, disp_buf, meta,
+                     slot_count, slot_offset, slot_rows, disp_row, ret_row, relay_buf, sp,
+                     MOE_STATIC_SCRATCH_BYTES, stream);
+  if (st != MOE_OK || !status) return st;
+  const DispatchScratch L = dispatch_scratch_layout(*g);
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const int32_t *)((const uint8_t *)sp + L.status), status);
+  return launch_status();
 }

@@ -265,6 +265,29 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
                     void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * moe_dispatch_q8_static -- moe_dispatch_q8 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same inputs, outputs, validation and errors as
+ * moe_dispatch_q8, but the scratch lives in a device array inside the library:
+ * MOE_STATIC_SCRATCH_BYTES on each GPU the library runs on, held until the
+ * process ends.  The call allocates nothing.
+ *   status   device int32 or NULL: receives the call's device status word
+ *            (MOE_DEVICE_* bits) when its kernels have run.
+ * Errors: those of moe_dispatch_q8; MOE_ERR_CAPACITY if the geometry needs more
+ * than MOE_STATIC_SCRATCH_BYTES of scratch (dispatch_scratch_bytes of
+ * moe_plan_sizes); MOE_ERR_HIP if the array's address cannot be obtained.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind
+ * (nothing in it needs to start cleared): calls on one GPU that overlap in time
+ * -- on different streams, or from different threads without ordering -- race.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+int moe_dispatch_q8_static(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
+                           const int32_t *slot_partition, uint32_t event_id, const moe_geom_t *g,
+                           void *disp_buf, moe_meta_t *meta, int32_t *slot_count,
+                           int32_t *slot_offset, int32_t *slot_rows, int32_t *disp_row,
+                           int32_t *ret_row, void *relay_buf, int32_t *status, void *stream);
+
+/*
  * moe_pack_expert_weights -- INT8 expert weights into the expert GEMMs' operand
  * image [XDS DeepSeek INT8 量化, P088: the routed experts' weights are stored
  * INT8; how they sit in memory is left open].  In the image, the weights that

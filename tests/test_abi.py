@@ -224,3 +224,19 @@ def test_eplb_planner_on_the_eplb_workload():
     assert np.array_equal(sl, o["slot_logical"]) and np.array_equal(sp, o["slot_partition"])
     assert sorted(sp[w.E:].tolist()) == list(range(w.E, w.E + w.budget))
     assert np.all(np.diff(o["tail"]) <= 1e-9)
+
+
+def test_static_dispatch_validation():
+    """The allocation-free dispatch refuses a geometry whose scratch exceeds its
+    static array, and invalid arguments, before any launch (no GPU needed)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    g = moe.geom(T=1 << 20, H=128, E=1024, P=1024, k=16, D=1024, Epp=1, S=1, LB=1 << 20)
+    assert moe.moe_plan_sizes(g, 0).dispatch_scratch_bytes > moe.MOE_STATIC_SCRATCH_BYTES
+    assert L.moe_dispatch_q8_static(fake, moe.DTYPE_BF16, fake, fake, 1, ctypes.byref(g), fake,
+                                    fake, fake, fake, fake, fake, fake, None, None,
+                                    None) == moe.MOE_ERR_CAPACITY
+    bad = moe.geom(T=16, H=100, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)  # H % 16 != 0
+    assert L.moe_dispatch_q8_static(fake, moe.DTYPE_BF16, fake, fake, 1, ctypes.byref(bad), fake,
+                                    fake, fake, fake, fake, fake, fake, None, None,
+                                    None) == moe.MOE_ERR_UNSUPPORTED
