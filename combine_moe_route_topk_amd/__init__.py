@@ -19,6 +19,7 @@ MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_CAPACITY = -3
+MOE_ERR_STALE = -4
 MOE_ERR_HIP = -5
 
 MOE_STATIC_SCRATCH_BYTES = 16 << 20  # the allocation-free dispatch's scratch per GPU
@@ -26,6 +27,7 @@ MOE_STATIC_SCRATCH_BYTES = 16 << 20  # the allocation-free dispatch's scratch pe
 MOE_DEVICE_BAD_ROUTE = 1
 MOE_DEVICE_BAD_PARTITION = 2
 MOE_DEVICE_OVER_CAPACITY = 4
+MOE_DEVICE_STALE_EVENT = 8
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATING_SOFTMAX, GATING_SIGMOID = 0, 1
@@ -37,7 +39,7 @@ EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispa
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
             "moe_pack_expert_weights", "moe_router_topk", "moe_quant_returns_q8",
-            "moe_dispatch_q8_static", "moe_status_string")
+            "moe_dispatch_q8_static", "moe_check_event", "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -100,6 +102,8 @@ def lib():
         L.moe_relay_returns.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), _P, _P]
         L.moe_combine.argtypes = [_I32, _P, _P, _P, ctypes.POINTER(Geom), _I32, _P, _P]
         L.moe_quant_returns_q8.argtypes = [_P, _P, ctypes.POINTER(Geom), _P, _P]
+        L.moe_check_event.argtypes = [_P, _P, _P, _P, ctypes.POINTER(Geom), ctypes.c_uint32, _P,
+                                      _P]
         L.moe_dispatch_q8_static.argtypes = [_P, _I32, _P, _P, ctypes.c_uint32,
                                              ctypes.POINTER(Geom), _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P]
@@ -189,6 +193,15 @@ def moe_dispatch_q8(x, x_dtype: int, phys_ids, slot_partition, event_id: int, g:
                                  _ptr(disp_row), _ptr(ret_row), _ptr(relay_buf), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream)),
            "moe_dispatch_q8")
+
+
+def moe_check_event(meta, disp_buf, slot_rows, slot_offset, g: Geom, event_id: int, status,
+                    stream=None):
+    """Writes MOE_DEVICE_STALE_EVENT to the device int32 `status` if any meta entry or
+    routed message trailer carries another event id, 0 otherwise (asynchronous)."""
+    _check(lib().moe_check_event(_ptr(meta), _ptr(disp_buf), _ptr(slot_rows), _ptr(slot_offset),
+                                 ctypes.byref(g), event_id & 0xFFFFFFFF, _ptr(status),
+                                 _stream(stream)), "moe_check_event")
 
 
 def moe_dispatch_q8_static(x, x_dtype: int, phys_ids, slot_partition, event_id: int, g: Geom,

@@ -26,6 +26,7 @@
 //   4. relay    (two-hop only) second hop: relay region rows -> final region.
 // No atomics decide any order: every row index is a deterministic function of
 // the routes, so the layout is bit-identical run to run.
+#include <algorithm>
 #include <atomic>
 
 #include "common.h"
@@ -486,6 +487,34 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
   return MOE_OK;
 }
 
+__global__ void clear_status_kernel(int32_t *__restrict__ status) {
+  if (threadIdx.x == 0) *status = 0;
+}
+
+// The receiver's event check: meta entries first, then the trailers of the
+// routed rows (event_lo is the top half of the trailer's last word).
+__global__ __launch_bounds__(256) void check_event_kernel(
+    const moe_meta_t *__restrict__ meta, int64_t nmeta, const uint8_t *__restrict__ disp_buf,
+    int64_t msg, int H, const int32_t *__restrict__ slot_rows,
+    const int32_t *__restrict__ slot_offset, int P, uint32_t event_id,
+    int32_t *__restrict__ status) {
+  const int64_t n = slot_offset[P];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool stale = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nmeta + n; i += stride) {
+    if (i < nmeta) {
+      stale |= meta[i].event_id != event_id;
+    } else {
+      const int32_t dr = slot_rows[i - nmeta];
+      if (dr >= 0) {
+        const uint32_t tw = *(const uint32_t *)(disp_buf + (int64_t)dr * msg + H + 12);
+        stale |= (tw >> 16) != (event_id & 0xffffu);
+      }
+    }
+  }
+  if (stale) atomicOr(status, MOE_DEVICE_STALE_EVENT);
+}
+
 // Copies the device status word of a dispatch into the caller's int32.
 __global__ void copy_status_kernel(const int32_t *__restrict__ src, int32_t *__restrict__ dst) {
   if (threadIdx.x == 0) *dst = *src;
@@ -545,5 +574,24 @@ extern "C" int moe_dispatch_q8_static(const void *x, moe_dtype_t x_dtype, const 
   const DispatchScratch L = dispatch_scratch_layout(*g);
   hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
                      (const int32_t *)((const uint8_t *)sp + L.status), status);
+  return launch_status();
+}
+
+extern "C" int moe_check_event(const moe_meta_t *meta, const void *disp_buf,
+                               const int32_t *slot_rows, const int32_t *slot_offset,
+                               const moe_geom_t *g, uint32_t event_id, int32_t *status,
+                               void *stream) {
+  int st = validate_geom(g);
+  if (st != MOE_OK) return st;
+  if (!meta || !slot_offset || !status) return MOE_ERR_INVALID_ARG;
+  if (g->T > 0 && (!disp_buf || !slot_rows)) return MOE_ERR_INVALID_ARG;
+  const int64_t nmeta = (int64_t)g->D * g->S;
+  const int64_t work = nmeta + (int64_t)g->T * g->k;
+  const unsigned blocks = (unsigned)std::min<int64_t>(1024, (work + 255) / 256);
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, status);
+  if ((st = launch_status()) != MOE_OK) return st;
+  hipLaunchKernelGGL(check_event_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, meta,
+                     nmeta, (const uint8_t *)disp_buf, msg_bytes_of(*g), g->H, slot_rows,
+                     slot_offset, g->P, event_id, status);
   return launch_status();
 }

@@ -189,6 +189,7 @@ extern "C" const char *moe_status_string(int s) {
     case MOE_ERR_INVALID_ARG: return "invalid argument";
     case MOE_ERR_UNSUPPORTED: return "unsupported geometry";
     case MOE_ERR_CAPACITY: return "capacity exceeded";
+    case MOE_ERR_STALE: return "stale event (metadata or messages of another dispatch)";
     case MOE_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }

@@ -9,11 +9,13 @@ Nothing here computes: it allocates with torch and calls the library.
 """
 from __future__ import annotations
 
+import os
 from typing import Optional
 
 import torch
 
-from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, PROJ_DOWN, PROJ_GATEUP,
+from . import (DTYPE_BF16, DTYPE_F32, GATING_SIGMOID, GATING_SOFTMAX, MOE_DEVICE_STALE_EVENT,
+               MOE_ERR_STALE, PROJ_DOWN, PROJ_GATEUP, MoeError, moe_check_event,
                RET_BF16, RET_Q8_BLOCKS, RET_Q8_FROM_DISPATCH, RET_Q8_ROWS, Geom, geom, moe_combine,
                moe_dispatch_q8, moe_expert_down_q8, moe_expert_down_q8_int8ret, moe_expert_ffn_q8,
                moe_expert_gateup_q8, moe_pack_expert_weights, moe_plan_sizes, moe_quant_returns_q8,
@@ -129,13 +131,24 @@ class MoeBuffers:
         return int(self.dscratch[:4].view(torch.int32).item())
 
 
+def _debug_checks_default() -> bool:
+    return os.environ.get("MOE_DEBUG_CHECKS", "0") not in ("", "0")
+
+
 class MoeLayer:
-    """One MoE layer: replica map + (optional) INT8 SwiGLU expert weights."""
+    """One MoE layer: replica map + (optional) INT8 SwiGLU expert weights.
+
+    With debug_checks (default: the MOE_DEBUG_CHECKS environment variable), the
+    experts and the combine first run the receiver's event check (moe_check_event)
+    on the dispatch's metadata and messages, wait for it, and raise MoeError with
+    MOE_ERR_STALE if they belong to another dispatch event."""
 
     def __init__(self, g: Geom, gating: str, slot_partition: torch.Tensor,
                  slot_logical: torch.Tensor, replica_offsets: Optional[torch.Tensor] = None,
                  replica_slots: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
-                 weights=None, I: int = 0, out_dtype: torch.dtype = torch.bfloat16):
+                 weights=None, I: int = 0, out_dtype: torch.dtype = torch.bfloat16,
+                 debug_checks: Optional[bool] = None):
+        self.debug_checks = _debug_checks_default() if debug_checks is None else debug_checks
         self.g = g
         if gating not in ("softmax", "sigmoid"):
             raise ValueError(f"gating {gating!r}: 'softmax' or 'sigmoid'")
@@ -215,7 +228,21 @@ class MoeLayer:
                         b.disp_buf, b.meta, b.slot_count, b.slot_offset, b.slot_rows, b.disp_row,
                         b.ret_row, b.relay_buf, b.dscratch)
 
+    def check_event(self):
+        """The receiver's event check (moe_check_event) against this layer's last
+        dispatch; raises MoeError(MOE_ERR_STALE) on a mismatch.  Synchronizes."""
+        b = self.buf
+        if getattr(self, "_ev_status", None) is None:
+            self._ev_status = torch.empty(1, dtype=torch.int32, device=b.meta.device)
+        status = self._ev_status
+        moe_check_event(b.meta, b.disp_buf, b.slot_rows, b.slot_offset, self.g, self.event_id,
+                        status)
+        if int(status.item()) & MOE_DEVICE_STALE_EVENT:
+            raise MoeError(MOE_ERR_STALE, "moe_check_event")
+
     def experts(self, acc_gateup_dbg=None, acc_down_dbg=None):
+        if self.debug_checks:
+            self.check_event()
         b = self.buf
         wgu, sgu, wd, sd = self.weights
         moe_expert_ffn_q8(b.disp_buf, b.slot_count, b.slot_offset, b.slot_rows, self.slot_logical,
@@ -223,6 +250,8 @@ class MoeLayer:
                           b.fscratch)
 
     def experts_gateup(self):
+        if self.debug_checks:
+            self.check_event()
         b = self.buf
         wgu, sgu, _, _ = self.weights
         moe_expert_gateup_q8(b.disp_buf, b.slot_count, b.slot_offset, b.slot_rows,
@@ -251,6 +280,8 @@ class MoeLayer:
         """mode 'q8' (identity experts: dispatched messages), 'bf16' (bf16 returns),
         'q8blocks' (INT8 returns of experts_down_int8ret) or 'q8rows' (token-wise INT8
         returns of quant_returns)."""
+        if self.debug_checks:
+            self.check_event()
         b = self.buf
         odt = DTYPE_BF16 if self.out_dtype == torch.bfloat16 else DTYPE_F32
         if mode == "q8":

@@ -57,6 +57,7 @@ enum {
   MOE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, inconsistent geometry   */
   MOE_ERR_UNSUPPORTED = -2, /* outside the limits below                         */
   MOE_ERR_CAPACITY = -3,    /* scratch too small / replica plan does not fit    */
+  MOE_ERR_STALE = -4,       /* metadata or messages of another dispatch event   */
   MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed              */
 };
 
@@ -64,7 +65,9 @@ enum {
 enum {
   MOE_DEVICE_BAD_ROUTE = 1,    /* physical slot id outside [0, P)                 */
   MOE_DEVICE_BAD_PARTITION = 2, /* slot_partition[p] outside [0, D)               */
-  MOE_DEVICE_OVER_CAPACITY = 4  /* a (d, s) region would exceed cap rows          */
+  MOE_DEVICE_OVER_CAPACITY = 4, /* a (d, s) region would exceed cap rows          */
+  MOE_DEVICE_STALE_EVENT = 8    /* moe_check_event: an event id that is not the   */
+                                /* expected one (meta or a message trailer)       */
 };
 
 /* limits */
@@ -263,6 +266,26 @@ int moe_dispatch_q8(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
                     void *disp_buf, moe_meta_t *meta, int32_t *slot_count, int32_t *slot_offset,
                     int32_t *slot_rows, int32_t *disp_row, int32_t *ret_row, void *relay_buf,
                     void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * moe_check_event -- the receiver's event check of the dispatch protocol
+ * [XDS 合设 MoE-Attention 的 All-to-All, P039-P040: each sender's metadata
+ * carries an event id, so that a receiver consumes only data of the current
+ * step].  Checks, on the device, that every meta[d][s].event_id equals
+ * event_id and that every message row listed in slot_rows[0 .. slot_offset[P])
+ * (the rows the expert FFN gathers and the INT8 combine reads) carries
+ * event_id & 0xffff in its trailer.  *status receives MOE_DEVICE_STALE_EVENT if
+ * anything mismatches, 0 otherwise.  The debug mode of the layer
+ * (MOE_DEBUG_CHECKS) runs it before the experts and before the combine and
+ * turns the bit into MOE_ERR_STALE.  Rows whose slot_rows entry is -1 (routes
+ * dropped by the dispatch) are skipped.
+ *   meta [D][S], disp_buf, slot_rows [T*k], slot_offset [P+1] as written by
+ *   moe_dispatch_q8;  status: device int32, written by this call.
+ * Errors: MOE_ERR_INVALID_ARG (NULL pointers), geometry errors.
+ */
+int moe_check_event(const moe_meta_t *meta, const void *disp_buf, const int32_t *slot_rows,
+                    const int32_t *slot_offset, const moe_geom_t *g, uint32_t event_id,
+                    int32_t *status, void *stream);
 
 /*
  * moe_dispatch_q8_static -- moe_dispatch_q8 for callers that cannot allocate

@@ -240,3 +240,15 @@ def test_static_dispatch_validation():
     assert L.moe_dispatch_q8_static(fake, moe.DTYPE_BF16, fake, fake, 1, ctypes.byref(bad), fake,
                                     fake, fake, fake, fake, fake, fake, None, None,
                                     None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_check_event_validation_and_status_string():
+    """moe_check_event refuses NULL pointers before any launch; MOE_ERR_STALE has a name."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    g = moe.geom(T=16, H=256, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+    assert L.moe_check_event(None, fake, fake, fake, ctypes.byref(g), 1, fake,
+                             None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_check_event(fake, fake, fake, fake, ctypes.byref(g), 1, None,
+                             None) == moe.MOE_ERR_INVALID_ARG
+    assert "stale" in moe.status_string(moe.MOE_ERR_STALE)

@@ -459,6 +459,54 @@ def test_twohop46080_e2a_combine_full_size():
     assert_close(bf16_to_f32(out[tsel]), bf16_to_f32(ref2), BF16_RTOL, BF16_ATOL, "end to end")
 
 
+def test_stale_event_detected():
+    """The receiver's event check of the dispatch protocol (XDS P039-P040): the
+    current dispatch's metadata and messages pass; metadata of an older dispatch,
+    an expected id the buffers do not carry, or one message trailer of another
+    event set the stale bit (the kernels end normally); the layer's debug mode
+    turns it into MOE_ERR_STALE, and a fresh dispatch clears the condition."""
+    c = Case(RAGGED)
+    w = c.w
+    c.layer.route(c.lg_d)
+    b = c.layer.buf
+    c.layer.event_id = 10
+    c.layer.dispatch(c.x_d)  # event 11
+    old_meta = b.meta.clone()
+    c.layer.dispatch(c.x_d)  # event 12
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def check(meta, ev):
+        status.fill_(-1)  # the call writes the word
+        moe.moe_check_event(meta, b.disp_buf, b.slot_rows, b.slot_offset, c.g, ev, status)
+        torch.cuda.synchronize()
+        return int(host(status)[0])
+
+    assert check(b.meta, 12) == 0
+    assert check(old_meta, 12) == moe.MOE_DEVICE_STALE_EVENT
+    assert check(b.meta, 13) == moe.MOE_DEVICE_STALE_EVENT
+    # one routed row whose trailer carries the previous event (metadata current)
+    row = int(host(b.slot_rows)[7])
+    v = b.disp_rows_view()
+    saved = v[row, w.H + 14:w.H + 16].clone()
+    v[row, w.H + 14] = 11
+    v[row, w.H + 15] = 0
+    assert check(b.meta, 12) == moe.MOE_DEVICE_STALE_EVENT
+    # the layer in debug mode refuses to consume them
+    c.layer.debug_checks = True
+    with pytest.raises(moe.MoeError) as err:
+        c.layer.combine("q8")
+    assert err.value.status == moe.MOE_ERR_STALE
+    v[row, w.H + 14:w.H + 16] = saved
+    c.layer.combine("q8")  # the same dispatch, restored: passes
+    c.layer.event_id = 20  # the caller thinks a later dispatch ran
+    with pytest.raises(moe.MoeError):
+        c.layer.combine("q8")
+    c.layer.dispatch(c.x_d)  # event 21: consistent again
+    c.layer.combine("q8")
+    torch.cuda.synchronize()
+    assert b.device_status() == 0
+
+
 def test_dispatch_is_deterministic():
     c = Case(RAGGED)
     c.layer.route(c.lg_d)
