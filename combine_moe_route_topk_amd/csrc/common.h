@@ -5,64 +5,10 @@
 #include <stdint.h>
 
 #include "moe_route_topk.h"
+#include "sizes.h"
 
 namespace moe {
 
-// ----------------------------------------------------------- host side ---
-
-inline int64_t msg_bytes_of(const moe_geom_t &g) {
-  return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 127) / 128) * 128;
-}
-inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
-// K splits of the router GEMM (bf16 [T][H] x [E][H]^T): 4 when the 128-row x
-// 256-expert tiles alone fill the GPU, more for small T (up to 32, and at
-// least one 64-byte K step per split); 0 = H not a multiple of 32.
-inline int router_splits(const moe_geom_t &g) {
-  const int64_t tiles = (((int64_t)g.T + 127) / 128) * ((g.E + 255) / 256);
-  int ks = 4;
-  while (ks < 32 && tiles * ks < 256) ks *= 2;
-  while (ks > 1 && g.H % (32 * ks) != 0) ks /= 2;
-  return g.H % 32 == 0 ? ks : 0;
-}
-inline int64_t router_scratch_bytes_of(const moe_geom_t &g) {
-  return (int64_t)router_splits(g) * g.T * g.E * 4;
-}
-// INT8 return row: H codes, then one fp32 scale per MOE_RET_Q8_BLOCK columns.
-// Rows are whole 128-byte cache lines, so that every 256-column block of codes
-// a GEMM tile stores covers whole lines (a row of H + 4 nblk bytes rounded only
-// to 16 would leave most blocks straddling lines, written partially by two tiles)
-inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
-  const int64_t nblk = ((int64_t)g.H + MOE_RET_Q8_BLOCK - 1) / MOE_RET_Q8_BLOCK;
-  return ((int64_t)g.H + 4 * nblk + 127) / 128 * 128;
-}
-
-// Image of the INT8 expert weights (moe_pack_expert_weights): one 16 KB block
-// per (expert, n-tile, 64-byte K step), n-tiles of 128 gate/up pairs
-// (gate/up) or 256 output channels (down), K padded to whole groups of four
-// steps.
-constexpr int64_t kPackedStepBytes = 256 * 64;
-__host__ __device__ inline int packed_ntiles(int proj, int H, int I) {
-  return proj == MOE_PROJ_GATEUP ? (I + 127) / 128 : (H + 255) / 256;
-}
-__host__ __device__ inline int packed_ksteps(int K) { return (K / 64 + 3) & ~3; }
-inline int64_t packed_weight_bytes(int proj, int E, int H, int I) {
-  const int K = proj == MOE_PROJ_GATEUP ? H : I;
-  return (int64_t)E * packed_ntiles(proj, H, I) * packed_ksteps(K) * kPackedStepBytes;
-}
-
-// Routes per dispatch chunk: chunks never straddle a source partition.
-constexpr int kChunkRoutes = 256;
-inline int chunk_tokens(const moe_geom_t &g) {
-  int ct = kChunkRoutes / g.k;
-  ct = ct < g.LB ? ct : g.LB;
-  return ct > 0 ? ct : 1;
-}
-inline int64_t chunks_per_source(const moe_geom_t &g) {
-  int ct = chunk_tokens(g);
-  return ((int64_t)g.LB + ct - 1) / ct;
-}
-
-int validate_geom(const moe_geom_t *g);
 // Gate logits as router_splits(g) partial sums [splits][T][E] (ffn_q8.hip), and
 // the host checks shared by the two gate entry points.
 int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *part,
@@ -73,28 +19,6 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 inline int launch_status() { return hip_status(hipGetLastError()); }
-
-// Byte layout of the dispatch scratch (all offsets 256-aligned).
-struct DispatchScratch {
-  int64_t status;       // int32 device status word, then the scan's int32 completion counter
-  int64_t hist_d;       // int32 [D][NC+1]  per-chunk route counts per destination partition
-  int64_t hist_p;       // int32 [P][NC+1]  per-chunk route counts per slot
-  int64_t route_rank;   // int32 [T*k]    (rank in chunk for d) | (rank in chunk for p) << 16
-  int64_t slot_local;   // int32 [P]
-  int64_t total;
-};
-DispatchScratch dispatch_scratch_layout(const moe_geom_t &g);
-
-// Byte layout of the expert-FFN scratch.
-struct FfnScratch {
-  int64_t tiles;     // int32 [P + 1]: exclusive prefix of per-slot m-tile counts, then the total
-  int64_t pmax;      // fp32 [T*k][I/64]  max |h| of each row over each gate-up n-tile
-  int64_t h;         // fp32 [T*k][I]
-  int64_t hq;        // int8 [T*k][I]
-  int64_t hs;        // fp32 [T*k]
-  int64_t total;
-};
-FfnScratch ffn_scratch_layout(const moe_geom_t &g, int32_t I);
 
 // ---------------------------------------------------------- device side ---
 

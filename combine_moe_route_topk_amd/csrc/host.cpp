@@ -1,11 +1,11 @@
-// Host-only parts of the C ABI: geometry validation, static sizing, scratch
-// layouts, the EPLB replica planner and status strings.
+// Host-only parts of the C ABI (plain C++, no HIP): geometry validation, static
+// sizing, scratch layouts, the EPLB replica planner and status strings.
 #include <algorithm>
 #include <cmath>
 #include <limits>
 #include <vector>
 
-#include "common.h"
+#include "sizes.h"
 
 namespace moe {
 
