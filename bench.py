@@ -397,6 +397,12 @@ def attainable(w, reps=5):
 
     ms = best(lambda: dst.copy_(src))
     out["copy_GBps"] = round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)
+    # one-direction ceilings: a 1 GiB fill (writes only) and a 1 GiB sum (reads only);
+    # the dispatch writes 4x what it reads, the combine reads 8x what it writes
+    ms = best(lambda: dst.fill_(2.0))
+    out["write_GBps"] = round(COPY_BYTES / (ms * 1e-3) / 1e9, 1)
+    ms = best(lambda: src.sum())
+    out["read_GBps"] = round(COPY_BYTES / (ms * 1e-3) / 1e9, 1)
     del src, dst
     M, K, N = w.T * w.k, w.H, 2 * w.I
     try:
