@@ -1,21 +1,28 @@
-"""Build-time check of the expert GEMMs' untracked weight loads.
+"""Build-time check of the expert GEMMs' untracked loads.
 
-The expert GEMM kernels load their weights with inline-assembly vector loads
-that the compiler does not track (its wait-count pass cannot follow a register
-ring across the loop edge).  They are correct only if the generated code never
-touches a load's destination registers before the data has landed; the
-kernel's own waits guarantee landing at the MFMA that consumes a buffer.  This
-module compiles the kernels to assembly and runs a dataflow analysis over each
-kernel's control-flow graph, with the set of pending registers (loaded, not
-yet consumed) as the state:
+The expert GEMM kernels load their weights with inline-assembly vector loads,
+and read their LDS fragments with inline-assembly ``ds_read_b128``; the
+compiler tracks neither (its wait-count pass cannot follow a register ring
+across the loop edge, and would order a tracked LDS read after every DMA in
+flight).  They are correct only if the generated code never touches a load's
+destination registers before the data has landed.  For a weight load the
+kernel's own waits guarantee landing at the MFMA that consumes the buffer; for
+an LDS read, at the kernel's explicit ``lgkmcnt(0)``.  This module compiles the
+kernels to assembly and runs a dataflow analysis over each kernel's
+control-flow graph, with the set of pending registers (loading, not yet
+consumed or waited for) as the state:
 
-  * an inline-assembly ``global_load_dwordx4`` adds its destination registers
-    (they must not be pending already, nor its address registers);
-  * a ``v_mfma`` reading pending registers as sources consumes them (its
-    destination must not be pending);
-  * ``s_waitcnt vmcnt(0)`` clears the set (everything has landed);
+  * an inline-assembly ``global_load_dwordx4`` or ``ds_read_b128`` adds its
+    destination registers (they must not be pending already, nor its address
+    registers);
+  * a ``v_mfma`` reading pending weight-load registers as sources consumes
+    them (its destination must not be pending, and none of its sources may be
+    a pending LDS read);
+  * ``s_waitcnt vmcnt(0)`` clears the pending weight loads, an ``s_waitcnt``
+    with ``lgkmcnt(0)`` the pending LDS reads;
   * any other instruction that reads or writes a pending register is a
-    violation, and so is a pending register at ``s_endpgm``;
+    violation (a copy or a spill would take the value before it lands), and so
+    is a pending register at ``s_endpgm``;
   * at control-flow joins the sets are united, iterated to a fixed point.
 
 ``check()`` raises on any violation; the library's build calls it, so a build
@@ -93,33 +100,49 @@ def _blocks(ins):
 
 
 def _step(t: str, is_asm: bool, pending: set, bad: list, name: str) -> set:
+    """One instruction's effect on the pending set: ("vm", r) for a register an
+    untracked global load is filling, ("lds", r) for one an untracked LDS read is
+    filling."""
     if t.endswith(":"):
         return pending
     op, args = _operands(t)
-    if op == "s_waitcnt" and "vmcnt(0)" in t:
-        return set()
+    if op == "s_waitcnt":
+        if "vmcnt(0)" in t:
+            pending = {p for p in pending if p[0] != "vm"}
+        if "lgkmcnt(0)" in t:
+            pending = {p for p in pending if p[0] != "lds"}
+        return pending
     if op == "s_endpgm":
         if pending:
-            bad.append(f"{name}: registers {sorted(pending)[:8]}... still loading at s_endpgm")
+            bad.append(f"{name}: registers {_names(pending)} still loading at s_endpgm")
         return pending
-    if is_asm and op == "global_load_dwordx4":
+    regs = {r for _, r in pending}
+    if is_asm and op in ("global_load_dwordx4", "ds_read_b128"):
         dst, addr = _regs(args[0]), _regs(args[1])
-        if (dst | addr) & pending:
-            bad.append(f"{name}: '{t}' while {sorted((dst | addr) & pending)[:8]} are still loading")
-        return pending | dst
-    touched = _regs(t) & pending
+        if (dst | addr) & regs:
+            bad.append(f"{name}: '{t}' while {sorted((dst | addr) & regs)[:8]} are still loading")
+        kind = "vm" if op.startswith("global") else "lds"
+        return {p for p in pending if p[1] not in dst} | {(kind, r) for r in dst}
+    touched = _regs(t) & regs
     if not touched:
         return pending
-    if op.startswith("v_mfma") and not (_regs(args[0]) & pending):
-        return pending - touched  # consumed: the kernel's waits make the data land here
-    bad.append(f"{name}: '{t}' touches {sorted(touched)[:8]} before the load into them is consumed")
-    return pending - touched
+    hit = {p for p in pending if p[1] in touched}
+    if (op.startswith("v_mfma") and not (_regs(args[0]) & regs)
+            and all(k == "vm" for k, _ in hit)):
+        return pending - hit  # consumed: the kernel's waits make the data land here
+    bad.append(f"{name}: '{t}' touches {_names(hit)} before the load into them is "
+               + ("waited for" if any(k == "lds" for k, _ in hit) else "consumed"))
+    return pending - hit
+
+
+def _names(pending) -> str:
+    return str(sorted(f"{k}:v{r}" for k, r in pending)[:8])
 
 
 def check_kernel(name: str, lines) -> list:
     """Violations (strings) in one kernel's assembly."""
     ins = _instructions(lines)
-    if not any(a and t.startswith("global_load_dwordx4") for t, a in ins):
+    if not any(a and t.startswith(("global_load_dwordx4", "ds_read_b128")) for t, a in ins):
         return []
     # the control-flow graph below knows direct branches only
     for t, _ in ins:
@@ -179,4 +202,4 @@ def check(hipcc: str, flags: list, src: str, include_dirs: list) -> None:
         subprocess.run(cmd, check=True, capture_output=True)
         bad = check_asm(asm)
     if bad:
-        raise RuntimeError("expert GEMM weight-load check failed:\n  " + "\n  ".join(bad[:20]))
+        raise RuntimeError("expert GEMM untracked-load check failed:\n  " + "\n  ".join(bad[:20]))

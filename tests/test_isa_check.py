@@ -1,8 +1,9 @@
-"""The build's check of the expert GEMMs' untracked weight loads, on small
-synthetic assembly listings: it must pass a load consumed by an MFMA, and catch
-each way the invariant can break (a touch before consumption, a copy, a reload
-into a pending register, a path that skips the consumer, a load still pending
-at the end), and accept a vmcnt(0) drain."""
+"""The build's check of the expert GEMMs' untracked loads, on small synthetic
+assembly listings: it must pass a weight load consumed by an MFMA and an LDS
+read used after lgkmcnt(0), and catch each way the invariant can break (a touch
+before consumption or the wait, a copy, a spill, a reload into a pending
+register, a path that skips the consumer or the wait, a load still pending at
+the end), and accept a vmcnt(0) drain."""
 import pytest
 
 from combine_moe_route_topk_amd.isa_check import check_kernel
@@ -59,6 +60,35 @@ def test_loop_carried_ring():
     assert bad(broken)
 
 
+DS = [";;#ASMSTART", "ds_read_b128 v[40:43], v8", ";;#ASMEND"]
+LGKM0 = ["s_waitcnt lgkmcnt(0)"]
+
+
+def test_lds_read_used_after_lgkmcnt0_is_clean():
+    assert bad(LOAD + DS + ["v_add_u32_e32 v5, v6, v7"] + LGKM0 + MFMA + END) == []
+    assert bad(DS + ["s_waitcnt vmcnt(0) lgkmcnt(0)", "v_mov_b32_e32 v50, v41"] + END) == []
+
+
+def test_lds_read_touched_before_lgkmcnt0():
+    assert bad(LOAD + DS + MFMA + LGKM0 + END)                           # the MFMA reads it early
+    assert bad(LOAD + DS + ["v_mov_b32_e32 v50, v41"] + LGKM0 + MFMA + END)  # a planted copy
+    assert bad(LOAD + DS + ["scratch_store_dwordx4 off, v[40:43], s0"] + LGKM0 + MFMA + END)
+    assert bad(LOAD + DS + ["s_waitcnt lgkmcnt(1)", "v_mov_b32_e32 v50, v41"] + LGKM0 + MFMA + END)
+    assert bad(LOAD + DS + ["s_waitcnt vmcnt(0)"] + MFMA + LGKM0 + END)  # vmcnt does not cover LDS
+
+
+def test_lds_read_reload_and_address_clobber():
+    assert bad(DS + DS + LGKM0 + END)
+    assert bad(DS + [";;#ASMSTART", "ds_read_b128 v[60:63], v41", ";;#ASMEND"] + LGKM0 + END)
+    assert bad(LOAD + [";;#ASMSTART", "ds_read_b128 v[60:63], v11", ";;#ASMEND"] + LGKM0 + MFMA + END)
+
+
+def test_lds_read_on_a_path_that_skips_the_wait():
+    lines = DS + ["s_cbranch_scc1 .LBB0_2"] + LGKM0 + [".LBB0_2:", "v_mov_b32_e32 v50, v40"] + END
+    assert bad(lines)
+    assert bad(DS + END)
+
+
 @pytest.mark.parametrize("n", [1])
 def test_the_built_kernels_have_weight_loads_to_check(n, tmp_path):
     """The real expert GEMMs, compiled to assembly: weight loads present, no violation."""
@@ -75,4 +105,5 @@ def test_the_built_kernels_have_weight_loads_to_check(n, tmp_path):
                    check=True, capture_output=True)
     text = open(asm).read()
     assert text.count("global_load_dwordx4") >= 6 * 16   # six GEMM variants, 16+ loads each
+    assert text.count("ds_read_b128") >= 6 * 8           # and their LDS fragment reads
     assert check_asm(asm) == []
