@@ -201,6 +201,7 @@ def time_router(layer, x, w, steps, warmup):
     nbytes = w.T * w.H * 2 + w.E * w.H * 2 + w.T * w.E * 4
     return {"us": round(us, 2), "TFLOPS": round(flops / (us * 1e-6) / 1e12, 1),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "splits": int(layer.buf.sizes.router_scratch_bytes // (w.T * w.E * 4)),
             "gate_and_topk_us": {"two_calls": round(two, 2), "fused": round(fused, 2)},
             "note": "bf16 MFMA, fp32 accumulation; timed alone (the workload's step starts "
@@ -551,6 +552,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline step (for counter runs: every launch of a "
                          "kernel then has the headline shape)")
+    ap.add_argument("--router-only", action="store_true",
+                    help="time only the gate logits (moe_router_logits, moe_router_topk) on "
+                         "the workload's hidden states: every gate launch then has that shape")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
@@ -571,6 +575,11 @@ def main():
     w = mw.WORKLOADS[args.workload]
     A = algorithmic(w)
     layer, x, lg = build_layer(w)
+    if args.router_only:
+        r = time_router(layer, x, w, args.steps, args.warmup)
+        log(f"[bench] router logits: {r['us']:.1f} us")
+        print(json.dumps({"workload": w.name, "router": r}), flush=True)
+        return
     ms, per, dist = time_gpu(layer, x, lg, args.steps, args.warmup)
     log(f"[bench] {ms:.3f} ms/step " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in per.items()))
 
@@ -664,7 +673,7 @@ def main():
     # the microbatch pipeline: two halves of the sources on two streams
     result["microbatch_pipeline"] = time_pipeline(layer, x, lg, w, args.steps, args.warmup)
     log(f"[bench] 2-microbatch pipeline: {result['microbatch_pipeline']['ms_per_step']:.3f} ms/step")
-    # the gate's logits from the hidden states (bf16 MFMA, split-K), timed alone:
+    # the gate's logits from the hidden states (bf16 MFMA), timed alone:
     # the headline step starts from the logits, as the workload defines
     result["router"] = time_router(layer, x, w, args.steps, args.warmup)
     log(f"[bench] router logits: {result['router']['us']:.1f} us")

@@ -44,13 +44,14 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    # the expert GEMMs' untracked weight loads: check the generated assembly
+    # the GEMMs' untracked weight and LDS loads: check the generated assembly
     # before the library is installed; a failing build leaves no library
     from .isa_check import check
     asm_flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
     try:
-        check(HIPCC, asm_flags, os.path.join(PKG, "csrc", "ffn_q8.hip"),
-              [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")])
+        for src in ("ffn_q8.hip", "router.hip"):
+            check(HIPCC, asm_flags, os.path.join(PKG, "csrc", src),
+                  [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")])
     except Exception:
         for f in (LIB + ".tmp", LIB):
             if os.path.exists(f):

@@ -9,9 +9,10 @@
 
 namespace moe {
 
-// Gate logits as router_splits(g) partial sums [splits][T][E] (ffn_q8.hip), and
-// the host checks shared by the two gate entry points.
-int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *part,
+// Gate logits into out (router.hip): [T][E] when router_splits(g) == 1, else
+// the partial sums [splits][T][E]; and the host checks shared by the two gate
+// entry points.
+int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *out,
                     hipStream_t s);
 int router_check(const void *x, const void *w_router, const moe_geom_t *g, void *scratch,
                  size_t scratch_bytes);

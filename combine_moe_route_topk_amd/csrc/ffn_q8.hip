@@ -29,8 +29,6 @@
 // contiguous stretch of it: the m-tiles of a group share every weight tile in
 // that XCD's L2.  Weight tiles that only one block reads, and the outputs,
 // move as non-temporal accesses so that they do not evict the shared tiles.
-// (The gate logits, a bf16 GEMM in the same kernel, keep a three-stage LDS
-// ring for both operands, two steps ahead.)
 #include <type_traits>
 
 #include "common.h"
@@ -40,8 +38,6 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BN = 256, BK = 64;
 #define MOE_LDS __attribute__((address_space(3)))
@@ -54,24 +50,21 @@ constexpr int LDS_STRIDE = BK;  // bytes per LDS row
 // m-tiles per group: gate/up 4 (its A rows, 7 KB each, are the bigger
 // operand to keep in L2: 1.4% faster than 8 on the Zipf layer), down 8
 template <int MODE> constexpr int kGroupM = MODE == 0 /* GATEUP */ ? 4 : 8;
-// LDS arena: three stages of (A + B) rows -- the gate logits' ring, DMA two K
-// steps ahead; the INT8 projections hold their four A stages in it
-constexpr int kStages = 3;
+// LDS arena of a block (72 KB): the four A stages of the main loop, then the
+// epilogue's staging tile
+constexpr int kArena = 3 * (BM + BN) * BK;
 // epilogue staging: fp32 rows of 128 + 8 values (the row scans' 16 lanes, 8
 // rows x 2 float4 columns, land on distinct bank groups; a stride of 128 + 4
 // spreads the staging writes further but conflicts there, and measured slower)
 // and bf16 rows of 256 values + 32 bytes
 constexpr int kStageStride = 128 + 8;
 constexpr int kStageStrideB = 2 * 256 + 32;
-static_assert(128 * kStageStride * 4 <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
-static_assert(128 * kStageStrideB <= kStages * (BM + BN) * BK, "staging fits the LDS arena");
+static_assert(128 * kStageStride * 4 <= kArena, "staging fits the LDS arena");
+static_assert(128 * kStageStrideB <= kArena, "staging fits the LDS arena");
 constexpr int kXcds = 8;
 
-// GATEUP, DOWN: the INT8 expert projections.  ROUTER: the gate's bf16 logits
-// x . W_router^T (bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation); a
-// 32-byte K sub-step holds 16 bf16 elements, so the operand movement and
-// layout are the same as for INT8.
-enum Mode { GATEUP = 0, DOWN = 1, ROUTER = 2 };
+// GATEUP, DOWN: the two INT8 expert projections.
+enum Mode { GATEUP = 0, DOWN = 1 };
 
 // ------------------------------------------------------------------ prep ---
 __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restrict__ slot_count,
@@ -148,7 +141,7 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 // Block tile 128 x 256, four wavefronts side by side along N, each owning all
 // 128 rows x 64 columns (4 x 2 MFMA 32x32 blocks, 128 accumulators): the four
 // waves share every A fragment read from LDS.  The loads of step kt + 2 are in
-// flight while step kt feeds the MFMAs (also in ROUTER mode); one barrier
+// flight while step kt feeds the MFMAs; one barrier
 // per K step; two blocks per CU overlap each other's waits.
 // Q8OUT (DOWN only): the return rows are INT8 with one fp32 scale per 256
 // columns (the n-tile) instead of bf16 -- see the epilogue.
@@ -162,50 +155,25 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     float *__restrict__ h_out, float *__restrict__ pmax, uint16_t *__restrict__ ret,
     int64_t ret_row_bytes, int32_t *__restrict__ acc_dbg) {
   constexpr int MB = BM / 32, NB = 2;       // MFMA blocks per wave
-  // one LDS arena: the K-step ring (A stages, then B stages) during the main
-  // loop, then the output staging of the epilogue
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (BM + BN) * LDS_STRIDE];
-  auto lds_a = [&](int st) { return lds + st * BM * LDS_STRIDE; };
-  auto lds_b = [&](int st) { return lds + kStages * BM * LDS_STRIDE + st * BN * LDS_STRIDE; };
+  // one LDS arena: the ring of A stages during the main loop, then the
+  // output staging of the epilogue
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kArena];
   __shared__ float row_scale[BM];
 
-  // ROUTER reuses the arguments: disp_buf = x (bf16 [nrows][H]), w = W_router
-  // (bf16 [E][H]), P = number of K splits, h_out = partial logits
-  // [P][nrows][E] (fp32); its K is the byte length of one split.
-  const int K = MODE == GATEUP ? H : MODE == DOWN ? I : 2 * H / P;
+  const int K = MODE == GATEUP ? H : I;
   const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
   Tile tl;
-  int e = 0, rows_here = 0, ksplit = 0;
-  int64_t row0 = 0;
-  if constexpr (MODE == ROUTER) {
-    // tiles ordered (split, n-tile, m-tile) so that the blocks of one XCD
-    // stretch share one split's slice of W_router in their L2
-    const int MT = (int)((nrows + BM - 1) / BM), NTR = (E + BN - 1) / BN;
-    const int64_t total = (int64_t)MT * NTR * P;
-    const int64_t per = (total + kXcds - 1) / kXcds;
-    const int64_t i = blockIdx.x / kXcds;
-    if (i >= per) return;
-    const int64_t L = (blockIdx.x % kXcds) * per + i;
-    if (L >= total) return;
-    tl.p = 0;
-    tl.m = (int)(L % MT);
-    tl.n = (int)((L / MT) % NTR);
-    ksplit = (int)(L / ((int64_t)MT * NTR));
-    row0 = (int64_t)tl.m * BM;
-    rows_here = (int)min((int64_t)BM, nrows - row0);
-  } else {
-    if (!decode_tile<kGroupM<MODE>>(tiles, slot_count, P, NT, tl)) return;
-    e = slot_logical[tl.p];
-    if (e < 0 || e >= E) return;
-    const int cnt = slot_count[tl.p];
-    row0 = (int64_t)slot_offset[tl.p] + (int64_t)tl.m * BM;  // first dense row
-    rows_here = min(BM, cnt - tl.m * BM);
-  }
+  if (!decode_tile<kGroupM<MODE>>(tiles, slot_count, P, NT, tl)) return;
+  const int e = slot_logical[tl.p];
+  if (e < 0 || e >= E) return;
+  const int cnt = slot_count[tl.p];
+  const int64_t row0 = (int64_t)slot_offset[tl.p] + (int64_t)tl.m * BM;  // first dense row
+  const int rows_here = min(BM, cnt - tl.m * BM);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // per-row scale of this tile (activation scale s_x, or hs)
-  if (MODE != ROUTER && tid < BM) {
+  if (tid < BM) {
     float sc = 0.0f;
     const int64_t rr = row0 + tid;
     if (tid < rows_here && rr < nrows) {
@@ -221,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 
   // Global -> LDS by DMA (global_load_lds_dwordx4): each wavefront instruction
   // fills one 1 KB LDS chunk = 16 tile rows x 64 bytes, lane i landing at
-  // chunk + 16 i.  Wave w fills A chunks 2w, 2w + 1 and B chunks 4w .. 4w + 3.
+  // chunk + 16 i.  Wave w fills A chunks 2w and 2w + 1.
   // Lane i covers row 16 q + i / 4 of chunk q and picks the source chunk
   // (i & 3) ^ ((row >> 2) & 3), which produces the swizzled layout above.
   // Tile rows past the slot's last row read a valid stand-in row instead, as
@@ -238,12 +206,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       const int32_t dr = slot_rows[rr];
       return disp_buf + (int64_t)(dr >= 0 ? dr : 0) * msg + c;
     }
-    if (MODE == ROUTER) return disp_buf + rr * 2 * H + (int64_t)ksplit * K + c;
     return (const uint8_t *)hq + rr * I + c;
-  };
-  auto b_row_ptr = [&](int r) -> const uint8_t * {  // W_router rows (ROUTER only)
-    const int c = ((lane & 3) ^ ((r >> 2) & 3)) * 16;
-    return (const uint8_t *)w + (int64_t)min(tl.n * BN + r, E - 1) * 2 * H + (int64_t)ksplit * K + c;
   };
   const uint8_t *pa0 = a_row_ptr(16 * (2 * wv) + lrow), *pa1 = a_row_ptr(16 * (2 * wv + 1) + lrow);
   // A: the DMA of one K step (wave w: A chunks 2w, 2w + 1) into an LDS stage
@@ -254,12 +217,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     __builtin_amdgcn_global_load_lds(pa1 + off, (MOE_LDS void *)(la + 1024), 16, 0, 0);
   };
 
-  // B-tile rows of this wave's two 32-column blocks
-  const int nbo0 = MODE == GATEUP ? wave * 32 : wave * 64;
-  const int nbo1 = MODE == GATEUP ? BN / 2 + wave * 32 : wave * 64 + 32;
-
-  using AccT = std::conditional_t<MODE == ROUTER, v16f, v16i>;
-  AccT acc[MB][NB];
+  v16i acc[MB][NB];
 #pragma unroll
   for (int a = 0; a < MB; ++a)
 #pragma unroll
@@ -273,67 +231,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // start at multiples of 32, so the swizzle depends on the lane only)
   const int koff0 = ((0 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
   const int koff1 = ((2 ^ (((lane & 31) >> 2) & 3)) ^ (lane >> 5)) * 16;
-  if constexpr (MODE == ROUTER) {
-    // Per K step: every wave waits until its own DMA of this step has landed
-    // (the DMA of the next step may still be in flight) and meets the others at
-    // the barrier, so the step's LDS stage is complete and the stage read one
-    // step ago is free; it reads all of the step's fragments, starts the DMA
-    // two steps ahead into that free stage, then runs the 16 MFMAs.
-    // B: W_router rows, this wave's B chunks 4w .. 4w + 3 of the step
-    const uint8_t *pb[4];
-  #pragma unroll
-    for (int c = 0; c < 4; ++c) pb[c] = b_row_ptr(16 * (4 * wv + c) + lrow);
-    auto dma = [&](int kstep, int buf) {
-      const int64_t off = (int64_t)kstep * BK;
-      dma_a(kstep, lds_a(buf));
-      uint8_t *lb = lds_b(buf) + 4 * wv * 1024;
-  #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_global_load_lds(pb[c] + off, (MOE_LDS void *)(lb + c * 1024), 16, 0, 0);
-    };
-    dma(0, 0);
-    if (KT > 1) dma(1, 1);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt % kStages;
-      if (kt + 1 < KT)
-        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): all but the next step's 6 DMAs
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      // fragment reads as raw ds_read_b128: the compiler's wait-count pass would
-      // otherwise order them after every DMA in flight (vmcnt(0)), undoing the
-      // ring; the explicit lgkmcnt(0) below makes the results safe to use.
-      const uint32_t la = lds_addr(lds_a(cur)) + (lane & 31) * LDS_STRIDE;
-      const uint32_t lb = lds_addr(lds_b(cur)) + (lane & 31) * LDS_STRIDE;
-      v4i bf[2][2], af[2][MB];
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t koff = ks ? koff1 : koff0;
-        bf[ks][0] = ds_read16(lb + nbo0 * LDS_STRIDE + koff);
-        bf[ks][1] = ds_read16(lb + nbo1 * LDS_STRIDE + koff);
-  #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) af[ks][mb] = ds_read16(la + mb * 32 * LDS_STRIDE + koff);
-      }
-      if (kt + 2 < KT) dma(kt + 2, (kt + 2) % kStages);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragments are in registers
-      __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMAs
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-  #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (mb >= mb_live) break;  // 32-row blocks past the slot's rows: nothing to compute
-          if constexpr (MODE == ROUTER) {
-            const v8bf a = __builtin_bit_cast(v8bf, af[ks][mb]);
-            acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][0]), acc[mb][0], 0, 0, 0);
-            acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, bf[ks][1]), acc[mb][1], 0, 0, 0);
-          } else {
-            acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][0], acc[mb][0], 0, 0, 0);
-            acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mb], bf[ks][1], acc[mb][1], 0, 0, 0);
-          }
-        }
-      }
-    }
-  } else {
+  {
     // B straight from the packed image into registers, two K steps ahead, in a
     // ring of four register buffers: each wavefront reads only its own 64
     // columns, 4 KB per step as four 1 KB runs in MFMA fragment order (the image
@@ -351,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     // steps ahead measured faster than three (2-3%; one step ahead is slower):
     // more loads in flight only queue longer.
     constexpr int kDepth = 2, kAStages = 4;
-    static_assert(kAStages * BM * LDS_STRIDE <= kStages * (BM + BN) * LDS_STRIDE, "A ring fits");
+    static_assert(kAStages * BM * LDS_STRIDE <= kArena, "A ring fits");
     const int KTp = (KT + 3) & ~3;
     const uint8_t *bsrc = (const uint8_t *)w + ((int64_t)e * NT + tl.n) * KTp * kPackedStepBytes +
                           wv * 4096 + lane * 16;
@@ -461,26 +359,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // (the weights are the MFMA's first operand).  Results go through an LDS
   // staging tile (fp32 h [128][128], or bf16 [128][256]), each lane writing
   // its runs of four consecutive columns at once, and leave as 16-byte vector
-  // stores of whole rows.  ROUTER keeps the other operand order: see there.
+  // stores of whole rows.
   const int col = lane & 31, half = lane >> 5;
-  if constexpr (MODE == ROUTER) {
-    // partial logits of this K split: acc[mb][nb][r] is tile row
-    // mb*32 + 8*(r/4) + 4*half + r%4, column wave*64 + nb*32 + col; a half
-    // wave stores 32 consecutive fp32 (one 128-byte line) per register
-    float *part = h_out + (int64_t)ksplit * nrows * E;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int c = tl.n * BN + wave * 64 + nb * 32 + col;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (lr < rows_here && c < E) part[(row0 + lr) * E + c] = acc[mb][nb][r];
-        }
-    }
-    return;
-  } else {
   float *stg = (float *)lds;
   if (MODE == GATEUP) {
     // acc[mb][0][r] / acc[mb][1][r]: gate / up of token row mb*32 + col and of
@@ -680,7 +560,6 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
             (v4i *)(ret + rr * H + n0 + c8));
     }
   }
-  }  // MODE != ROUTER
 }
 
 // ---------------------------------------------------------------- requant ---
@@ -736,25 +615,6 @@ __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restric
     if (c < n4) dst[c] = code4(v[q]);
   }
   for (int c = kRequantMaxI / 4 + lane; c < n4; c += 64) dst[c] = code4(src[c]);
-}
-
-// ------------------------------------------------------- router reduce ---
-// logits = sum of the K-split partial logits, in split order (fixed, so the
-// result does not depend on scheduling); n = T * E, a multiple of 4.
-__global__ __launch_bounds__(256) void router_reduce_kernel(const float *__restrict__ part,
-                                                            int64_t n, int splits,
-                                                            float *__restrict__ logits) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  float4 a = *(const float4 *)(part + i);
-  for (int sp = 1; sp < splits; ++sp) {
-    const float4 b = *(const float4 *)(part + (int64_t)sp * n + i);
-    a.x = a.x + b.x;
-    a.y = a.y + b.y;
-    a.z = a.z + b.z;
-    a.w = a.w + b.w;
-  }
-  *(float4 *)(logits + i) = a;
 }
 
 // ------------------------------------------------------- weight packing ---
@@ -944,54 +804,6 @@ extern "C" int moe_expert_ffn_q8(const void *disp_buf, const int32_t *slot_count
   if (st != MOE_OK) return st;
   return moe_expert_down_q8(slot_count, slot_offset, slot_logical, w_down, s_down, I, g, ret,
                             acc_down_dbg, scratch, scratch_bytes, stream);
-}
-
-namespace moe {
-
-// Partial gate logits of the router_splits(g) K splits into part [splits][T][E]
-// (fp32); the caller has validated the geometry, pointers and scratch size.
-int router_partials(const void *x, const void *w_router, const moe_geom_t &g, float *part,
-                    hipStream_t s) {
-  const int ks = router_splits(g);
-  const int64_t mt = ((int64_t)g.T + BM - 1) / BM, nt = (g.E + BN - 1) / BN;
-  const int64_t blocks = (mt * nt * ks + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((ffn_gemm_kernel<ROUTER, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const int32_t *)nullptr, (const int32_t *)nullptr, (const int32_t *)nullptr,
-                     (const int32_t *)nullptr, (const int32_t *)nullptr, (const uint8_t *)x,
-                     (int64_t)0, (const int8_t *)nullptr, (const float *)nullptr,
-                     (const int8_t *)w_router, (const float *)nullptr, ks, g.E, g.H, 0,
-                     (int64_t)g.T, part, (float *)nullptr, (uint16_t *)nullptr, (int64_t)0,
-                     (int32_t *)nullptr);
-  return launch_status();
-}
-
-int router_check(const void *x, const void *w_router, const moe_geom_t *g, void *scratch,
-                 size_t scratch_bytes) {
-  int st = validate_geom(g);
-  if (st != MOE_OK) return st;
-  if (router_splits(*g) == 0 || g->E % 4 != 0) return MOE_ERR_UNSUPPORTED;
-  if (g->T == 0) return MOE_OK;
-  if (!x || !w_router || !scratch) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(scratch)) return MOE_ERR_INVALID_ARG;
-  if ((int64_t)scratch_bytes < router_scratch_bytes_of(*g)) return MOE_ERR_CAPACITY;
-  return MOE_OK;
-}
-
-}  // namespace moe
-
-extern "C" int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g,
-                                 float *logits, void *scratch, size_t scratch_bytes,
-                                 void *stream) {
-  int st = router_check(x, w_router, g, scratch, scratch_bytes);
-  if (st != MOE_OK || g->T == 0) return st;
-  if (!logits || !aligned16(logits)) return MOE_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  float *part = (float *)scratch;
-  if ((st = router_partials(x, w_router, *g, part, s)) != MOE_OK) return st;
-  const int64_t n = (int64_t)g->T * g->E;
-  hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                     part, n, router_splits(*g), logits);
-  return launch_status();
 }
 
 extern "C" int moe_pack_expert_weights(const int8_t *w, moe_proj_t proj, int32_t E, int32_t H,

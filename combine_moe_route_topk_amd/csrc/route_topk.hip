@@ -332,10 +332,14 @@ extern "C" int moe_router_topk(const void *x, const void *w_router, const float 
   int st = route_check(gating, replica_offsets, replica_slots, g, topk_ids, topk_w, phys_ids);
   if (st != MOE_OK) return st;
   if ((st = router_check(x, w_router, g, scratch, scratch_bytes)) != MOE_OK || g->T == 0) return st;
+  if (logits && !aligned16(logits)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  float *part = (float *)scratch;
+  // one split: the gate writes the logits themselves (the caller's, or scratch)
+  // and the top-k reads them; several: the top-k adds the partial sums
+  const int ks = router_splits(*g);
+  float *part = ks == 1 && logits ? logits : (float *)scratch;
   if ((st = router_partials(x, w_router, *g, part, s)) != MOE_OK) return st;
-  const RouteIn in{part, router_splits(*g), (int64_t)g->T * g->E, logits};
+  const RouteIn in{part, ks, (int64_t)g->T * g->E, ks == 1 ? nullptr : logits};
   return route_run(in, false, bias, gating, replica_offsets, replica_slots, g, topk_ids, topk_w,
                    phys_ids, expert_counts, s);
 }

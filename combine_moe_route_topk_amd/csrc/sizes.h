@@ -13,15 +13,20 @@ inline int64_t msg_bytes_of(const moe_geom_t &g) {
   return g.msg_bytes ? (int64_t)g.msg_bytes : (((int64_t)g.H + 16 + 127) / 128) * 128;
 }
 inline int64_t cap_of(const moe_geom_t &g) { return (int64_t)g.LB * (g.k < g.Epp ? g.k : g.Epp); }
-// K splits of the router GEMM (bf16 [T][H] x [E][H]^T): 4 when the 128-row x
-// 256-expert tiles alone fill the GPU, more for small T (up to 32, and at
-// least one 64-byte K step per split); 0 = H not a multiple of 32.
+// Router GEMM (bf16 [T][H] x [E][H]^T) tiles: 192 tokens x 256 experts, K
+// steps of 64 elements.  K splits: the largest divisor of the step count that
+// keeps tiles x splits <= 256 (one block per CU), at most 32; 0 = H not a
+// multiple of 64.
+constexpr int kRouterRows = 192, kRouterCols = 256, kRouterStep = 64;
 inline int router_splits(const moe_geom_t &g) {
-  const int64_t tiles = (((int64_t)g.T + 127) / 128) * ((g.E + 255) / 256);
-  int ks = 4;
-  while (ks < 32 && tiles * ks < 256) ks *= 2;
-  while (ks > 1 && g.H % (32 * ks) != 0) ks /= 2;
-  return g.H % 32 == 0 ? ks : 0;
+  if (g.H <= 0 || g.H % kRouterStep != 0) return 0;
+  const int64_t tiles = ((int64_t)g.T + kRouterRows - 1) / kRouterRows *
+                        ((g.E + kRouterCols - 1) / kRouterCols);
+  const int steps = g.H / kRouterStep;
+  int ks = 1;
+  for (int d = 2; d <= 32 && d <= steps; ++d)
+    if (steps % d == 0 && tiles * d <= 256) ks = d;
+  return ks;
 }
 inline int64_t router_scratch_bytes_of(const moe_geom_t &g) {
   return (int64_t)router_splits(g) * g.T * g.E * 4;

@@ -1,6 +1,6 @@
-"""Build-time check of the expert GEMMs' untracked loads.
+"""Build-time check of the GEMMs' untracked loads.
 
-The expert GEMM kernels load their weights with inline-assembly vector loads,
+The expert GEMM and gate GEMM kernels load their weights with inline-assembly vector loads,
 and read their LDS fragments with inline-assembly ``ds_read_b128``; the
 compiler tracks neither (its wait-count pass cannot follow a register ring
 across the loop edge, and would order a tracked LDS read after every DMA in
@@ -175,7 +175,10 @@ def check_kernel(name: str, lines) -> list:
     return sorted(set(bad_all))
 
 
-def check_asm(path: str, kernel_regex: str = r"ffn_gemm_kernel") -> list:
+KERNELS = r"(ffn_gemm_kernel|router_gemm_kernel)"
+
+
+def check_asm(path: str, kernel_regex: str = KERNELS) -> list:
     lines = open(path).read().splitlines()
     starts = [i for i, l in enumerate(lines)
               if re.match(r"^_Z\S*" + kernel_regex + r"\S*:", l)]
@@ -184,16 +187,17 @@ def check_asm(path: str, kernel_regex: str = r"ffn_gemm_kernel") -> list:
         end = next((j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end")),
                    len(lines))
         body = lines[i:end + 1]
-        if any("global_load_dwordx4" in l for l in body):
+        if any("global_load_dwordx4" in l or "ds_read_b128" in l for l in body):
             checked += 1
         bad += check_kernel(lines[i].split(":")[0], body)
     if checked == 0:
-        bad.append("no kernel with inline-assembly weight loads was found")
+        bad.append(f"{path}: no kernel with inline-assembly loads was found")
     return bad
 
 
 def check(hipcc: str, flags: list, src: str, include_dirs: list) -> None:
-    """Compile src to gfx950 assembly with the build's flags and check it."""
+    """Compile src to gfx950 assembly with the build's flags and check it (the
+    source must hold at least one kernel with such loads)."""
     with tempfile.TemporaryDirectory() as d:
         asm = os.path.join(d, "k.s")
         cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-o", asm, src]
@@ -202,4 +206,4 @@ def check(hipcc: str, flags: list, src: str, include_dirs: list) -> None:
         subprocess.run(cmd, check=True, capture_output=True)
         bad = check_asm(asm)
     if bad:
-        raise RuntimeError("expert GEMM untracked-load check failed:\n  " + "\n  ".join(bad[:20]))
+        raise RuntimeError("GEMM untracked-load check failed:\n  " + "\n  ".join(bad[:20]))

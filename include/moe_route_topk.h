@@ -197,15 +197,17 @@ int moe_route_topk(const void *logits, moe_dtype_t logits_dtype, const float *bi
  * "INT8：少搬一些": gating stays in BF16/FP32 while the matmuls go INT8; XDS
  * P038: dispatch and combine follow the gating scores]:
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h]
- * bf16 operands, products and sums in fp32 (MFMA), fp32 logits.  The sum over
- * h is split into router_splits parts whose partial sums are added in split
- * order, so the result is the same every run; its error against the exact
- * value is within the fp32 summation bound (H * 2^-24 * sum |x w|).  Feed
- * the logits to moe_route_topk (MOE_DTYPE_F32).
- *   x        [T][H] bf16, 16B;  w_router [E][H] bf16, 16B;  H % 32 == 0, E % 4 == 0
+ * bf16 operands, products and sums in fp32 (MFMA), fp32 logits.  Tiles of 96
+ * tokens x 128 experts; when they are too few to fill the GPU, the sum over h
+ * is split into router_splits parts (whole 64-element steps) whose partial
+ * sums are added in split order, so the result is the same every run; its
+ * error against the exact value is within the fp32 summation bound
+ * (H * 2^-24 * sum |x w|).  Feed the logits to moe_route_topk (MOE_DTYPE_F32).
+ *   x        [T][H] bf16, 16B;  w_router [E][H] bf16, 16B;  H % 64 == 0, E % 4 == 0
  *   logits   [T][E] fp32, 16B
- *   scratch  router_scratch_bytes (moe_plan_sizes), 16B
- * Errors: MOE_ERR_UNSUPPORTED (H % 32 or E % 4), MOE_ERR_CAPACITY (scratch),
+ *   scratch  router_scratch_bytes (moe_plan_sizes), 16B: the partial sums when
+ *            H is split (unused otherwise, but still required)
+ * Errors: MOE_ERR_UNSUPPORTED (H % 64 or E % 4), MOE_ERR_CAPACITY (scratch),
  * MOE_ERR_INVALID_ARG (NULL or misaligned pointers).
  */
 int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g, float *logits,
@@ -216,11 +218,11 @@ int moe_router_logits(const void *x, const void *w_router, const moe_geom_t *g, 
  * [CMI EP320 fused_moe listing: gate.topk(hidden, k = 8); XDS 专家负载均衡 P068
  * (the collect step) and P078-P079 (the replica gather)]: the logits of
  * moe_router_logits, then moe_route_topk on them (MOE_DTYPE_F32), without the
- * logits' round trip through memory: the top-k reads the gate's K-split partial
- * sums and adds them in split order itself, so logits, ids, weights, physical
- * ids and counts are the same bits as the two calls give.
+ * round trip of the summed logits when H is split: the top-k reads the gate's
+ * partial sums and adds them in split order itself.  Logits, ids, weights,
+ * physical ids and counts are the same bits as the two calls give.
  *   x, w_router, scratch  as moe_router_logits (router_scratch_bytes)
- *   logits   [T][E] fp32, or NULL when the caller does not keep them
+ *   logits   [T][E] fp32, 16B, or NULL when the caller does not keep them
  *   bias, gating, replica_offsets, replica_slots, topk_ids, topk_w, phys_ids,
  *   expert_counts  as moe_route_topk
  * Errors: those of the two calls.

@@ -124,10 +124,11 @@ def test_int8_returns_and_router_validation():
     assert L.moe_quant_returns_q8(None, fake, ctypes.byref(g), fake, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quant_returns_q8(fake, fake, ctypes.byref(g), ctypes.c_void_p(0x1004),
                                   None) == moe.MOE_ERR_INVALID_ARG
-    # router: H a multiple of 32, E a multiple of 4, scratch large enough, 16-byte alignment
-    odd_h = moe.geom(T=16, H=80, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
-    assert L.moe_router_logits(fake, fake, ctypes.byref(odd_h), fake, fake, 1 << 30,
-                               None) == moe.MOE_ERR_UNSUPPORTED
+    # router: H a multiple of 64, E a multiple of 4, scratch large enough, 16-byte alignment
+    for h in (80, 96):
+        odd_h = moe.geom(T=16, H=h, E=8, P=8, k=2, D=4, Epp=2, S=4, LB=4)
+        assert L.moe_router_logits(fake, fake, ctypes.byref(odd_h), fake, fake, 1 << 30,
+                                   None) == moe.MOE_ERR_UNSUPPORTED
     odd_e = moe.geom(T=16, H=256, E=6, P=6, k=2, D=3, Epp=2, S=4, LB=4)
     assert L.moe_router_logits(fake, fake, ctypes.byref(odd_e), fake, fake, 1 << 30,
                                None) == moe.MOE_ERR_UNSUPPORTED
@@ -135,10 +136,20 @@ def test_int8_returns_and_router_validation():
                                s.router_scratch_bytes - 1, None) == moe.MOE_ERR_CAPACITY
     assert L.moe_router_logits(ctypes.c_void_p(0x1008), fake, ctypes.byref(g), fake, fake,
                                1 << 30, None) == moe.MOE_ERR_INVALID_ARG
-    # split count: whole 64-byte K steps per split, more splits for few tokens
-    assert s.router_scratch_bytes % (16 * 8 * 4) == 0
-    splits = s.router_scratch_bytes // (16 * 8 * 4)
-    assert 4 <= splits <= 32 and (2 * 256) % (64 * splits) == 0
+    # split count: 192-token x 256-expert tiles; the largest divisor of the
+    # 64-element step count keeping tiles x splits <= 256 (at most 32);
+    # scratch = splits x T x E fp32
+    def splits(T, H, E):
+        gg = moe.geom(T=T, H=H, E=E, P=E, k=1, D=E, Epp=1, S=1, LB=T)
+        return moe.moe_plan_sizes(gg, 256).router_scratch_bytes // (T * E * 4)
+    assert splits(16, 256, 8) == 4                # 1 tile, 4 steps
+    assert splits(12288, 7168, 256) == 4          # 64 tiles x 4 = 256 blocks
+    assert splits(46080, 7168, 256) == 1          # 240 tiles
+    assert splits(4096, 7168, 256) == 8           # 22 tiles, 112 steps
+    assert splits(96, 7168, 256) == 28            # 1 tile: 28 of the 112 steps' divisors
+    assert splits(300, 384, 40) == 6              # 2 tiles, 6 steps: one step per split
+    assert splits(16, 64, 8) == 1                 # a single step
+    assert splits(4100, 192, 1020) == 1           # 88 tiles x 3 steps > 256
 
 
 def test_pack_expert_weights_validation_and_sizes():

@@ -152,8 +152,8 @@ def test_router_logits_and_topk(name):
     """Gate logits (bf16 MFMA, split-K, fixed-order reduction) within the fp32
     bound of the exact values; the top-k of the GPU's own fp32 logits is the
     oracle's top-k of the same logits bit for bit, and two runs give the same
-    bits.  ragged: T = 300 (a partial 128-row tile), E = 40 (a partial expert
-    tile); decode96: T = 96, 32 K splits."""
+    bits.  ragged: T = 300 (a partial 192-row tile), E = 40 (a partial expert
+    tile), 6 K splits of one step each; decode96: T = 96, 28 K splits of 4 steps."""
     w = RAGGED if name == "ragged" else mw.WORKLOADS["decode96"]
     c, got = _router_case(w)
     again = host(c.layer.router(c.x_d, dev_bits(mw.router_weights(w), True)))
@@ -190,6 +190,34 @@ def test_router_topk_fused_equals_two_calls(name):
             a = host(t)
             assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                   r.view(np.uint32) if r.dtype == np.float32 else r), label
+
+
+@pytest.mark.parametrize("T,H,E,splits", [(4100, 192, 1020, 1), (200, 6144, 128, 32)])
+def test_router_logits_tails(T, H, E, splits):
+    """The gate kernel's edges through the C ABI: partial token tiles (4100 = 21 x
+    192 + 68, 200 = 192 + 8), a partial expert tile (1020 = 3 x 256 + 252, and
+    128 of 256), three K steps per block (one split of 3 steps; 32 splits of 96
+    steps); logits within the fp32 bound of the exact values, and the same bits
+    on a second run."""
+    rng = np.random.default_rng(T + H + E)
+    x = mw.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    wr = mw.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) / np.float32(np.sqrt(H)))
+    g = moe.geom(T=T, H=H, E=E, P=E, k=1, D=E, Epp=1, S=1, LB=T)
+    sz = moe.moe_plan_sizes(g)
+    assert sz.router_scratch_bytes == splits * T * E * 4
+    scratch = torch.empty(sz.router_scratch_bytes // 4, dtype=torch.float32, device="cuda")
+    runs = []
+    for _ in range(2):
+        logits = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+        _log(f"moe_router_logits T={T} H={H} E={E}")
+        moe.moe_router_logits(dev_bits(x, True), dev_bits(wr, True), g, logits, scratch)
+        torch.cuda.synchronize()
+        runs.append(host(logits))
+    ref = oracle.router_logits(x, wr)
+    mag = oracle.router_logits(x & np.uint16(0x7FFF), wr & np.uint16(0x7FFF))
+    err = np.abs(runs[0].astype(np.float64) - ref)
+    assert np.all(err <= H * 2.0 ** -24 * mag + 1e-30), f"max err/bound {np.max(err / (H * 2.0 ** -24 * mag + 1e-30)):.3g}"
+    assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32)), "deterministic"
 
 
 def test_router_logits_layer12288_sampled_tokens():

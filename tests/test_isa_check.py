@@ -89,9 +89,11 @@ def test_lds_read_on_a_path_that_skips_the_wait():
     assert bad(DS + END)
 
 
-@pytest.mark.parametrize("n", [1])
-def test_the_built_kernels_have_weight_loads_to_check(n, tmp_path):
-    """The real expert GEMMs, compiled to assembly: weight loads present, no violation."""
+@pytest.mark.parametrize("src,loads,reads", [("ffn_q8.hip", 6 * 16, 6 * 8), ("router.hip", 0, 20)])
+def test_the_built_kernels_have_loads_to_check(src, loads, reads, tmp_path):
+    """The real GEMMs, compiled to assembly: the untracked loads are there, and no
+    violation (the expert GEMMs: six variants with weight loads and LDS fragment
+    reads; the gate GEMM: LDS fragment reads)."""
     import os
     import subprocess
     from combine_moe_route_topk_amd import build as B
@@ -101,9 +103,9 @@ def test_the_built_kernels_have_weight_loads_to_check(n, tmp_path):
     asm = str(tmp_path / "k.s")
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
     subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-o", asm,
-                    os.path.join(B.PKG, "csrc", "ffn_q8.hip"), "-I", os.path.join(B.ROOT, "include")],
+                    os.path.join(B.PKG, "csrc", src), "-I", os.path.join(B.ROOT, "include")],
                    check=True, capture_output=True)
     text = open(asm).read()
-    assert text.count("global_load_dwordx4") >= 6 * 16   # six GEMM variants, 16+ loads each
-    assert text.count("ds_read_b128") >= 6 * 8           # and their LDS fragment reads
+    assert text.count("global_load_dwordx4") >= loads
+    assert text.count("ds_read_b128") >= reads
     assert check_asm(asm) == []
