@@ -19,10 +19,12 @@
 //               histograms in (source, chunk) order.  For d this single prefix
 //               is both the receive layout offset of source s (its value at
 //               s's first chunk) and, relative to it, the chunk's base row in
-//               region (d, s); the d blocks write meta.  The last p block
-//               writes slot_offset / slot_local; the status word is cleared.
-//   3. scatter  one wavefront per token: amax, scale, IEEE divide + RNE to
-//               int8, 16-byte stores of the k message rows and trailers.
+//               region (d, s); the d blocks write meta, the p blocks
+//               slot_count / slot_local; the status word is cleared.
+//   3. scatter  every block first prefixes slot_count into the slots' first
+//               rows (block 0 stores them as slot_offset); then one wavefront
+//               per token: amax, scale, IEEE divide + RNE to int8, 16-byte
+//               stores of the k message rows and trailers.
 //   4. relay    (two-hop only) second hop: relay region rows -> final region.
 // No atomics decide any order: every row index is a deterministic function of
 // the routes, so the layout is bit-identical run to run.
@@ -62,7 +64,7 @@ __device__ __forceinline__ int bits_for(int n) {
 __global__ __launch_bounds__(256) void dispatch_count_kernel(
     const int32_t *__restrict__ phys, const int32_t *__restrict__ slot_partition, int T, int k,
     int P, int D, int LB, int ct, int cps, int nc, int32_t *__restrict__ hist_d,
-    int32_t *__restrict__ hist_p, int32_t *__restrict__ route_rank, int32_t *__restrict__ done) {
+    int32_t *__restrict__ hist_p, int32_t *__restrict__ route_rank) {
   extern __shared__ int32_t lds[];
   int32_t *wd = lds;              // [4][D]
   int32_t *wp = lds + 4 * D;      // [4][P]
@@ -73,7 +75,6 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
   const int n = (int)(t1 - t0) * k;
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * (D + P); i += 256) lds[i] = 0;
-  if (c == 0 && tid == 0) *done = 0;  // completion counter of the scan kernel that follows
   __syncthreads();
 
   const int64_t gi = t0 * k + tid;
@@ -134,19 +135,16 @@ __device__ __forceinline__ int block_incl_scan_256(int v, int *sh) {
 // Block b < D scans hist_d row b and writes meta[b][s] = {event, prefix at
 // s's first chunk, count} for every source s; block D + p scans hist_p row p
 // and writes slot_count[p] and slot_local[p].  Scans are exclusive over the nc
-// chunks, the total goes to column nc.  The last slot block to finish (an
-// agent-scope acquire-release counter, zeroed by the count kernel) prefixes
-// the slot totals into slot_offset; block 0 clears the status word, so no
-// separate finalize launch is needed.
+// chunks, the total goes to column nc.  Block 0 clears the status word.  The
+// slot totals' prefix (slot_offset) is taken by every scatter block from
+// slot_count, so no block here waits for the others.
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     int32_t *__restrict__ hist_d, int32_t *__restrict__ hist_p,
     const int32_t *__restrict__ slot_partition, int D, int P, int S, int cps, int nc,
     uint32_t event_id, moe_meta_t *__restrict__ meta, int32_t *__restrict__ slot_count,
-    int32_t *__restrict__ slot_offset, int32_t *__restrict__ slot_local,
-    int32_t *__restrict__ status, int32_t *__restrict__ done) {
+    int32_t *__restrict__ slot_local, int32_t *__restrict__ status) {
   __shared__ int sh[4];
   __shared__ int carry_sh;
-  __shared__ int last;
   const bool is_d = blockIdx.x < (unsigned)D;
   const int row = is_d ? blockIdx.x : blockIdx.x - D;
   int32_t *h = (is_d ? hist_d : hist_p) + (int64_t)row * (nc + 1);
@@ -186,26 +184,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     __syncthreads();
     if (threadIdx.x == 0) slot_local[row] = sh[0] + sh[1] + sh[2] + sh[3];
   }
-  if (threadIdx.x == 0) {
-    slot_count[row] = carry;
-    // release: this block's total is visible before the count goes up
-    last = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == P - 1;
-  }
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every slot block's total is visible
-  int off = 0;
-  for (int base = 0; base < P; base += 256) {
-    const int q = base + threadIdx.x;
-    const int v = q < P ? hist_p[(int64_t)q * (nc + 1) + nc] : 0;
-    const int incl = block_incl_scan_256(v, sh);
-    if (q < P) slot_offset[q] = off + incl - v;
-    if (threadIdx.x == 255) carry_sh = incl;
-    __syncthreads();
-    off += carry_sh;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) slot_offset[P] = off;
+  if (threadIdx.x == 0) slot_count[row] = carry;
 }
 
 // -------------------------------------------------------------- scatter ---
@@ -219,11 +198,35 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const void *__restrict__ x, const int32_t *__restrict__ phys,
     const int32_t *__restrict__ slot_partition, const int32_t *__restrict__ slot_local,
     const int32_t *__restrict__ hist_d, const int32_t *__restrict__ hist_p,
-    const int32_t *__restrict__ route_rank, const int32_t *__restrict__ slot_offset, int T,
-    int H, int k, int S, int LB, int ct, int cps, int nc, int64_t cap, int64_t msg, int relays,
-    uint32_t event_id, uint8_t *__restrict__ disp_buf, uint8_t *__restrict__ relay_buf,
+    const int32_t *__restrict__ route_rank, const int32_t *__restrict__ slot_count,
+    int32_t *__restrict__ slot_offset, int T, int H, int k, int S, int P, int LB, int ct,
+    int cps, int nc, int64_t cap, int64_t msg, int relays, uint32_t event_id,
+    uint8_t *__restrict__ disp_buf, uint8_t *__restrict__ relay_buf,
     int32_t *__restrict__ slot_rows, int32_t *__restrict__ disp_row,
     int32_t *__restrict__ ret_row, int32_t *__restrict__ status) {
+  // the slots' first dense rows: an exclusive prefix of slot_count (1 KB at
+  // P = 256, from L2), taken by every block; block 0 also stores it as
+  // slot_offset [P + 1]
+  __shared__ int32_t soff[MOE_MAX_P + 1];
+  __shared__ int sh[4];
+  __shared__ int carry_sh;
+  {
+    int carry = 0;
+    for (int base = 0; base < P; base += 256) {
+      const int q = base + threadIdx.x;
+      const int v = q < P ? slot_count[q] : 0;
+      const int incl = block_incl_scan_256(v, sh);
+      if (q < P) soff[q] = carry + incl - v;
+      if (threadIdx.x == 255) carry_sh = incl;
+      __syncthreads();
+      carry += carry_sh;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) soff[P] = carry;
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int q = threadIdx.x; q <= P; q += 256) slot_offset[q] = soff[q];
+  }
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       const int d = slot_partition[p];
       const int32_t *hd = hist_d + (int64_t)d * (nc + 1);
       const int64_t r = (int64_t)(hd[c] - hd[s * cps]) + (rr & 0xffff);
-      const int32_t rrow = slot_offset[p] + hist_p[(int64_t)p * (nc + 1) + c] + (rr >> 16);
+      const int32_t rrow = soff[p] + hist_p[(int64_t)p * (nc + 1) + c] + (rr >> 16);
       out_r = rrow;
       if (r >= cap) {
         atomicOr(status, MOE_DEVICE_OVER_CAPACITY);
@@ -391,17 +394,17 @@ __global__ void dispatch_empty_kernel(int D, int S, int P, uint32_t event_id,
 template <int NIT>
 void launch_scatter(bool bf16, dim3 grid, hipStream_t st, const void *x, const int32_t *phys,
                     const int32_t *sp, const int32_t *sl, const int32_t *hd, const int32_t *hp,
-                    const int32_t *rr, const int32_t *so, const moe_geom_t &g, int ct, int cps,
-                    int nc, int64_t cap, int64_t msg, uint32_t ev, uint8_t *db, uint8_t *rb,
-                    int32_t *srows, int32_t *drow, int32_t *rrow, int32_t *status) {
+                    const int32_t *rr, const int32_t *scount, int32_t *so, const moe_geom_t &g,
+                    int ct, int cps, int nc, int64_t cap, int64_t msg, uint32_t ev, uint8_t *db,
+                    uint8_t *rb, int32_t *srows, int32_t *drow, int32_t *rrow, int32_t *status) {
   if (bf16)
     hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, true>), grid, dim3(256), 0, st, x, phys, sp,
-                       sl, hd, hp, rr, so, g.T, g.H, g.k, g.S, g.LB, ct, cps, nc, cap, msg,
-                       g.relays, ev, db, rb, srows, drow, rrow, status);
+                       sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc, cap,
+                       msg, g.relays, ev, db, rb, srows, drow, rrow, status);
   else
     hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, false>), grid, dim3(256), 0, st, x, phys, sp,
-                       sl, hd, hp, rr, so, g.T, g.H, g.k, g.S, g.LB, ct, cps, nc, cap, msg,
-                       g.relays, ev, db, rb, srows, drow, rrow, status);
+                       sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc, cap,
+                       msg, g.relays, ev, db, rb, srows, drow, rrow, status);
 }
 
 }  // namespace
@@ -448,13 +451,12 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
   const int64_t cap = cap_of(*g), msg = msg_bytes_of(*g);
 
   const size_t lds = sizeof(int32_t) * 4 * (g->D + g->P);
-  int32_t *done = status + 1;  // scan completion counter, beside the status word
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nc), dim3(256), lds, s, phys_ids, slot_partition,
-                     g->T, g->k, g->P, g->D, g->LB, ct, cps, nc, hist_d, hist_p, route_rank, done);
+                     g->T, g->k, g->P, g->D, g->LB, ct, cps, nc, hist_d, hist_p, route_rank);
   if ((st = launch_status()) != MOE_OK) return st;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(g->D + g->P), dim3(256), 0, s, hist_d, hist_p,
                      slot_partition, g->D, g->P, g->S, cps, nc, event_id, meta, slot_count,
-                     slot_offset, slot_local, status, done);
+                     slot_local, status);
   if ((st = launch_status()) != MOE_OK) return st;
 
   const dim3 grid((unsigned)((g->T + 3) / 4));
@@ -463,8 +465,8 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
   const int nit = (g->H + 1023) / 1024;
 #define MOE_SCATTER(N)                                                                         \
   launch_scatter<N>(bf16, grid, s, x, phys_ids, slot_partition, slot_local, hist_d, hist_p,     \
-                    route_rank, slot_offset, *g, ct, cps, nc, cap, msg, event_id, db, rb,        \
-                    slot_rows, disp_row, ret_row, status)
+                    route_rank, slot_count, slot_offset, *g, ct, cps, nc, cap, msg, event_id, db, \
+                    rb, slot_rows, disp_row, ret_row, status)
   if (nit <= 1)
     MOE_SCATTER(1);
   else if (nit <= 2)
