@@ -70,7 +70,7 @@ int validate_geom(const moe_geom_t *g);
 
 // Byte layout of the dispatch scratch (all offsets 256-aligned).
 struct DispatchScratch {
-  int64_t status;       // int32 device status word, then the scan's int32 completion counter
+  int64_t status;       // int32 device status word (then one unused int32)
   int64_t hist_d;       // int32 [D][NC+1]  per-chunk route counts per destination partition
   int64_t hist_p;       // int32 [P][NC+1]  per-chunk route counts per slot
   int64_t route_rank;   // int32 [T*k]    (rank in chunk for d) | (rank in chunk for p) << 16
