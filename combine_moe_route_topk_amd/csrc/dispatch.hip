@@ -26,6 +26,9 @@
 //               per token: amax, scale, IEEE divide + RNE to int8, 16-byte
 //               stores of the k message rows and trailers.
 //   4. relay    (two-hop only) second hop: relay region rows -> final region.
+// Decode-size batches (at most 1024 routes, no relay hop) take one launch
+// instead (dispatch_small_kernel): the same layout, ranked in LDS by every
+// block, and one wavefront per 1024-element slice of a token.
 // No atomics decide any order: every row index is a deterministic function of
 // the routes, so the layout is bit-identical run to run.
 #include <algorithm>
@@ -193,7 +196,10 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
 // 16-byte int8 store per message copy.  The token rows are read once: bf16
 // rows come in by non-temporal loads (non-temporal stores of the messages
 // measured slower, ordinary stores are kept).
-template <int NIT, bool BF16>
+// PER_ROUTE (small batches, to spread them over the GPU): one wavefront per
+// route instead of per token; it quantizes its token exactly as the token's
+// wavefront would and writes that route's copy only.
+template <int NIT, bool BF16, bool PER_ROUTE>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const void *__restrict__ x, const int32_t *__restrict__ phys,
     const int32_t *__restrict__ slot_partition, const int32_t *__restrict__ slot_local,
@@ -204,6 +210,39 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     uint8_t *__restrict__ disp_buf, uint8_t *__restrict__ relay_buf,
     int32_t *__restrict__ slot_rows, int32_t *__restrict__ disp_row,
     int32_t *__restrict__ ret_row, int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = PER_ROUTE ? wv / k : wv;
+  const int jsel = PER_ROUTE ? (int)(wv % k) : 0;  // the wavefront's route (PER_ROUTE)
+  const bool live = t < T;
+  const bool mine = live && (PER_ROUTE ? lane == jsel : lane < k);  // lanes with a route
+
+  // ---- loads first: the token row and the routes' ranks and slots, whose
+  // latency then overlaps the slot prefix below and the lookups after it ----
+  uint4 raw[NIT][BF16 ? 2 : 4];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int e0 = (i * 64 + lane) * 16;
+    if (live && e0 < H) {
+      if (BF16) {
+        const v4u *src = (const v4u *)((const uint16_t *)x + t * H + e0);
+        const v4u a0 = __builtin_nontemporal_load(src), a1 = __builtin_nontemporal_load(src + 1);
+        raw[i][0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+        raw[i][1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+      } else {
+        const uint4 *src = (const uint4 *)((const float *)x + t * H + e0);
+#pragma unroll
+        for (int q = 0; q < (BF16 ? 2 : 4); ++q) raw[i][q] = src[q];
+      }
+    }
+  }
+  const int64_t gi = t * k + lane;
+  int rr = 0, p = 0;
+  if (mine) {
+    rr = route_rank[gi];
+    p = phys[gi];
+  }
+
   // the slots' first dense rows: an exclusive prefix of slot_count (1 KB at
   // P = 256, from L2), taken by every block; block 0 also stores it as
   // slot_offset [P + 1]
@@ -227,24 +266,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     if (blockIdx.x == 0)
       for (int q = threadIdx.x; q <= P; q += 256) slot_offset[q] = soff[q];
   }
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (!live) return;
   const int s = (int)(t / LB), b = (int)(t % LB);
   const int c = s * cps + b / ct;
 
-  // ---- per-route row indices (lanes 0..k-1) ----
+  // ---- per-route row indices (lanes 0..k-1, or the wavefront's route) ----
   int64_t drow = -1;
   int dpart = 0;
   uint32_t tail_w = 0;
-  if (lane < k) {
-    const int64_t gi = t * k + lane;
-    const int rr = route_rank[gi];
+  if (mine) {
     int32_t out_d = -1, out_r = -1;
     if (rr < 0) {
       atomicOr(status, rr == -1 ? MOE_DEVICE_BAD_ROUTE : MOE_DEVICE_BAD_PARTITION);
     } else {
-      const int p = phys[gi];
       const int d = slot_partition[p];
       const int32_t *hd = hist_d + (int64_t)d * (nc + 1);
       const int64_t r = (int64_t)(hd[c] - hd[s * cps]) + (rr & 0xffff);
@@ -266,18 +300,13 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     ret_row[gi] = out_r;
   }
 
-  // ---- load the token and quantize ----
-  uint4 raw[NIT][BF16 ? 2 : 4];
+  // ---- quantize ----
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < NIT; ++i) {
     const int e0 = (i * 64 + lane) * 16;
     if (e0 < H) {
       if (BF16) {
-        const v4u *src = (const v4u *)((const uint16_t *)x + t * H + e0);
-        const v4u a0 = __builtin_nontemporal_load(src), a1 = __builtin_nontemporal_load(src + 1);
-        raw[i][0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
-        raw[i][1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
         const uint32_t *w = (const uint32_t *)&raw[i][0];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -285,9 +314,6 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
           amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
         }
       } else {
-        const uint4 *src = (const uint4 *)((const float *)x + t * H + e0);
-#pragma unroll
-        for (int q = 0; q < (BF16 ? 2 : 4); ++q) raw[i][q] = src[q];
         const float *f = (const float *)&raw[i][0];
 #pragma unroll
         for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(f[q]));
@@ -334,7 +360,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
   // ---- k message copies ----
   const int64_t relay_base = (int64_t)relays * S * cap;
-  for (int j = 0; j < k; ++j) {
+  for (int j = jsel; j < (PER_ROUTE ? jsel + 1 : k); ++j) {
     const int64_t row = __shfl(drow, j, 64);
     if (row < 0) continue;
     const int d = __shfl(dpart, j, 64);
@@ -348,6 +374,251 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     }
     if (lane == 0)
       *(uint4 *)(dst + H) = make_uint4(__float_as_uint(scale), (uint32_t)s, (uint32_t)b, tw);
+  }
+}
+
+// -------------------------------------------------------- small batches ---
+// Decode-size batches (at most kSmallRoutes routes, D x S <= kSmallRegions,
+// no relay hop): count, scan and scatter in one launch.  Every block ranks all
+// T k routes in LDS: a route's row in region (d, s) is the number of valid
+// routes before it (route order t k + j) with the same d and s, and its slot
+// row the number before it with the same slot after the earlier slots'
+// totals -- the layout the three-kernel path builds from its chunk prefixes.
+// Wavefront w takes token w / ns and its 1024-element slice w % ns for all k
+// copies (the token's amax from a first pass over the whole row), so no
+// wavefront quantizes more than a slice.  Block 0 also writes meta, the slot
+// counts and offsets, and the status word: every error bit of the batch,
+// written whole (no other block touches it).
+constexpr int kSmallRoutes = 1024, kSmallRegions = 4096;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dispatch_small_kernel(
+    const void *__restrict__ x, const int32_t *__restrict__ phys,
+    const int32_t *__restrict__ slot_partition, int T, int H, int k, int S, int P, int D, int LB,
+    int ns, int64_t cap, int64_t msg, uint32_t event_id, uint8_t *__restrict__ disp_buf,
+    moe_meta_t *__restrict__ meta, int32_t *__restrict__ slot_count,
+    int32_t *__restrict__ slot_offset, int32_t *__restrict__ slot_rows,
+    int32_t *__restrict__ disp_row, int32_t *__restrict__ ret_row, int32_t *__restrict__ status) {
+  __shared__ int32_t kd[kSmallRoutes];    // region d S + s of each route; -2 bad slot, -3 bad partition
+  __shared__ int32_t kp[kSmallRoutes];    // slot of each valid route, else -1
+  __shared__ int32_t spart[MOE_MAX_P];    // slot_partition
+  __shared__ int32_t soff[MOE_MAX_P + 1]; // slot totals, then their exclusive prefix
+  __shared__ int32_t region[kSmallRegions];
+  __shared__ int sh[4];
+  __shared__ int carry_sh, bits_sh;
+  const int N = T * k;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  const int64_t t = wv / ns;
+  const int slice = (int)(wv % ns);
+  const bool live = t < T;
+
+  // ---- the layout, in every block ----
+  for (int q = tid; q < P; q += 256) {
+    spart[q] = slot_partition[q];
+    soff[q] = 0;
+  }
+  const bool b0 = blockIdx.x == 0;
+  if (b0)
+    for (int r = tid; r < D * S; r += 256) region[r] = 0;
+  if (tid == 0) bits_sh = 0;
+  __syncthreads();
+  int bits = 0;
+  for (int g = tid; g < N; g += 256) {
+    const int p = phys[g];
+    int keyd = -2, keyp = -1;
+    if (p >= 0 && p < P) {
+      const int d = spart[p];
+      if (d >= 0 && d < D) {
+        keyd = d * S + (g / k) / LB;
+        keyp = p;
+        atomicAdd(&soff[p], 1);
+        if (b0) atomicAdd(&region[keyd], 1);
+      } else {
+        keyd = -3;
+        bits |= MOE_DEVICE_BAD_PARTITION;
+      }
+    } else {
+      bits |= MOE_DEVICE_BAD_ROUTE;
+    }
+    kd[g] = keyd;
+    kp[g] = keyp;
+  }
+  if (b0 && bits) atomicOr(&bits_sh, bits);
+  __syncthreads();
+  {
+    int carry = 0;
+    for (int base = 0; base < P; base += 256) {
+      const int q = base + tid;
+      const int v = q < P ? soff[q] : 0;
+      const int incl = block_incl_scan_256(v, sh);
+      if (q < P) soff[q] = carry + incl - v;
+      if (tid == 255) carry_sh = incl;
+      __syncthreads();
+      carry += carry_sh;
+      __syncthreads();
+    }
+    if (tid == 0) soff[P] = carry;
+    __syncthreads();
+  }
+  if (b0) {
+    for (int q = tid; q <= P; q += 256) {
+      slot_offset[q] = soff[q];
+      if (q < P) slot_count[q] = soff[q + 1] - soff[q];
+    }
+    int over = 0;
+    for (int d = tid; d < D; d += 256) {
+      int off = 0;
+      for (int src = 0; src < S; ++src) {
+        const int c = region[d * S + src];
+        moe_meta_t m;
+        m.event_id = event_id;
+        m.offset = off;
+        m.count = c;
+        m.reserved = 0;
+        meta[(int64_t)d * S + src] = m;
+        off += c;
+        if (c > cap) over = MOE_DEVICE_OVER_CAPACITY;
+      }
+    }
+    if (over) atomicOr(&bits_sh, over);
+    __syncthreads();
+    if (tid == 0) *status = bits_sh;
+  }
+  // ---- ranks of this block's routes (its waves cover tokens t0 .. t1) ----
+  // nr routes, tpr threads each (a power of two, at least 4, within one
+  // wavefront): thread (r, seg) counts the matches among routes seg, seg + tpr,
+  // ... before route r, then the tpr partial counts are summed by shuffles
+  __shared__ int32_t rk_d[64], rk_p[64], rk_loc[64];
+  const int64_t t0 = (int64_t)blockIdx.x * 4 / ns;
+  const int64_t t1 = min(((int64_t)blockIdx.x * 4 + 3) / ns, (int64_t)T - 1);
+  const int nr = (int)(t1 - t0 + 1) * k;  // <= 4 k <= 64
+  int tpr = 64;
+  while (tpr > 4 && tpr * nr > 256) tpr >>= 1;
+  {
+    const int r = tid / tpr, seg = tid % tpr;
+    int cd = 0, cp = 0, cl = 0;
+    const int gr = (int)(t0 * k) + r;
+    const bool act = r < nr && gr < N;
+    const int kdr = act ? kd[gr] : -1, kpr = act ? kp[gr] : -1;
+    if (kdr >= 0) {
+      for (int g = seg; g < gr; g += tpr) {
+        cd += kd[g] == kdr;
+        cp += kp[g] == kpr;
+      }
+      const int dr = spart[kpr];
+      for (int q = seg; q < kpr; q += tpr) cl += spart[q] == dr;
+    }
+    for (int o = tpr >> 1; o > 0; o >>= 1) {
+      cd += __shfl_xor(cd, o, 64);
+      cp += __shfl_xor(cp, o, 64);
+      cl += __shfl_xor(cl, o, 64);
+    }
+    if (act && seg == 0) {
+      rk_d[r] = cd;
+      rk_p[r] = cp;
+      rk_loc[r] = cl;
+    }
+    __syncthreads();
+  }
+  if (!live) return;
+
+  // ---- the token's k routes (lane j: route j) ----
+  const int src_s = (int)(t / LB), bpos = (int)(t % LB);
+  int64_t drow = -1;
+  int32_t rrow = -1;
+  uint32_t tail_w = 0;
+  if (lane < k) {
+    const int gi = (int)(t * k + lane);
+    const int kdj = kd[gi], kpj = kp[gi];
+    if (kdj >= 0) {
+      const int r = gi - (int)(t0 * k);
+      const int cd = rk_d[r];
+      drow = cd < cap ? (int64_t)kdj * cap + cd : -1;
+      rrow = soff[kpj] + rk_p[r];
+      tail_w = (uint32_t)lane | ((uint32_t)(rk_loc[r] & 0xff) << 8) | ((event_id & 0xffffu) << 16);
+    }
+  }
+  if (slice == 0 && lane < k) {
+    const int64_t gi = t * k + lane;
+    if (rrow >= 0) slot_rows[rrow] = drow >= 0 ? (int32_t)drow : -1;
+    disp_row[gi] = drow >= 0 ? (int32_t)drow : -1;
+    ret_row[gi] = rrow;
+  }
+
+  // ---- amax over the row, then this wavefront's slice into every copy ----
+  float amax = 0.0f;
+  for (int i = 0; i * 1024 < H; ++i) {
+    const int e0 = (i * 64 + lane) * 16;
+    if (e0 < H) {
+      if (BF16) {
+        const v4u *sp = (const v4u *)((const uint16_t *)x + t * H + e0);
+        const v4u a0 = sp[0], a1 = sp[1];
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffffu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+        }
+      } else {
+        const float4 *fp = (const float4 *)((const float *)x + t * H + e0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = fp[q];
+          amax = fmaxf(amax, fabsf(f.x));
+          amax = fmaxf(amax, fabsf(f.y));
+          amax = fmaxf(amax, fabsf(f.z));
+          amax = fmaxf(amax, fabsf(f.w));
+        }
+      }
+    }
+  }
+  amax = wave_max_f32(amax);
+  const float scale = amax / 127.0f;
+  const int e0 = (slice * 64 + lane) * 16;
+  uint4 code = make_uint4(0u, 0u, 0u, 0u);
+  if (e0 < H) {
+    float v[16];
+    if (BF16) {
+      const v4u *sp = (const v4u *)((const uint16_t *)x + t * H + e0);
+      const v4u a0 = sp[0], a1 = sp[1];
+      const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+        v[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+      }
+    } else {
+      const float *f = (const float *)x + t * H + e0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = f[q];
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int c = 0;
+        if (scale != 0.0f) {
+          float y = rintf(v[4 * q + r] / scale);
+          y = fminf(fmaxf(y, -127.0f), 127.0f);
+          c = (int)y;
+        }
+        word |= ((uint32_t)c & 0xffu) << (8 * r);
+      }
+      pk[q] = word;
+    }
+    code = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int64_t row = __shfl(drow, j, 64);  // with every lane active
+    const uint32_t tw = __shfl(tail_w, j, 64);
+    if (row < 0) continue;
+    uint8_t *dst = disp_buf + row * msg;
+    if (e0 < H) *(uint4 *)(dst + e0) = code;
+    if (slice == 0 && lane == 0)
+      *(uint4 *)(dst + H) = make_uint4(__float_as_uint(scale), (uint32_t)src_s, (uint32_t)bpos, tw);
   }
 }
 
@@ -391,20 +662,39 @@ __global__ void dispatch_empty_kernel(int D, int S, int P, uint32_t event_id,
   }
 }
 
+template <int NIT, bool PR>
+void launch_scatter2(bool bf16, dim3 grid, hipStream_t st, const void *x, const int32_t *phys,
+                     const int32_t *sp, const int32_t *sl, const int32_t *hd, const int32_t *hp,
+                     const int32_t *rr, const int32_t *scount, int32_t *so, const moe_geom_t &g,
+                     int ct, int cps, int nc, int64_t cap, int64_t msg, uint32_t ev, uint8_t *db,
+                     uint8_t *rb, int32_t *srows, int32_t *drow, int32_t *rrow, int32_t *status) {
+  if (bf16)
+    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, true, PR>), grid, dim3(256), 0, st, x, phys,
+                       sp, sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc,
+                       cap, msg, g.relays, ev, db, rb, srows, drow, rrow, status);
+  else
+    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, false, PR>), grid, dim3(256), 0, st, x, phys,
+                       sp, sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc,
+                       cap, msg, g.relays, ev, db, rb, srows, drow, rrow, status);
+}
+
+// One wavefront per token, or per route when the tokens alone would give
+// fewer blocks than the GPU has CUs (decode batches).
 template <int NIT>
-void launch_scatter(bool bf16, dim3 grid, hipStream_t st, const void *x, const int32_t *phys,
+void launch_scatter(bool bf16, hipStream_t st, const void *x, const int32_t *phys,
                     const int32_t *sp, const int32_t *sl, const int32_t *hd, const int32_t *hp,
                     const int32_t *rr, const int32_t *scount, int32_t *so, const moe_geom_t &g,
                     int ct, int cps, int nc, int64_t cap, int64_t msg, uint32_t ev, uint8_t *db,
                     uint8_t *rb, int32_t *srows, int32_t *drow, int32_t *rrow, int32_t *status) {
-  if (bf16)
-    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, true>), grid, dim3(256), 0, st, x, phys, sp,
-                       sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc, cap,
-                       msg, g.relays, ev, db, rb, srows, drow, rrow, status);
+  const bool per_route = (g.T + 3) / 4 < 256;
+  const int64_t waves = per_route ? (int64_t)g.T * g.k : g.T;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (per_route)
+    launch_scatter2<NIT, true>(bf16, grid, st, x, phys, sp, sl, hd, hp, rr, scount, so, g, ct,
+                               cps, nc, cap, msg, ev, db, rb, srows, drow, rrow, status);
   else
-    hipLaunchKernelGGL((dispatch_scatter_kernel<NIT, false>), grid, dim3(256), 0, st, x, phys, sp,
-                       sl, hd, hp, rr, scount, so, g.T, g.H, g.k, g.S, g.P, g.LB, ct, cps, nc, cap,
-                       msg, g.relays, ev, db, rb, srows, drow, rrow, status);
+    launch_scatter2<NIT, false>(bf16, grid, st, x, phys, sp, sl, hd, hp, rr, scount, so, g, ct,
+                                cps, nc, cap, msg, ev, db, rb, srows, drow, rrow, status);
 }
 
 }  // namespace
@@ -441,6 +731,23 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
   hipStream_t s = (hipStream_t)stream;
   uint8_t *sc = (uint8_t *)scratch;
   int32_t *status = (int32_t *)(sc + L.status);
+  const int64_t cap = cap_of(*g), msg = msg_bytes_of(*g);
+  if (g->relays == 0 && (int64_t)g->T * g->k <= kSmallRoutes &&
+      (int64_t)g->D * g->S <= kSmallRegions) {
+    const int ns = (g->H + 1023) / 1024;
+    const dim3 grid((unsigned)(((int64_t)g->T * ns + 3) / 4));
+    if (x_dtype == MOE_DTYPE_BF16)
+      hipLaunchKernelGGL(dispatch_small_kernel<true>, grid, dim3(256), 0, s, x, phys_ids,
+                         slot_partition, g->T, g->H, g->k, g->S, g->P, g->D, g->LB, ns, cap, msg,
+                         event_id, (uint8_t *)disp_buf, meta, slot_count, slot_offset, slot_rows,
+                         disp_row, ret_row, status);
+    else
+      hipLaunchKernelGGL(dispatch_small_kernel<false>, grid, dim3(256), 0, s, x, phys_ids,
+                         slot_partition, g->T, g->H, g->k, g->S, g->P, g->D, g->LB, ns, cap, msg,
+                         event_id, (uint8_t *)disp_buf, meta, slot_count, slot_offset, slot_rows,
+                         disp_row, ret_row, status);
+    return launch_status();
+  }
   int32_t *hist_d = (int32_t *)(sc + L.hist_d);
   int32_t *hist_p = (int32_t *)(sc + L.hist_p);
   int32_t *route_rank = (int32_t *)(sc + L.route_rank);
@@ -448,7 +755,6 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
   const int ct = chunk_tokens(*g);
   const int cps = (int)chunks_per_source(*g);
   const int nc = g->S * cps;
-  const int64_t cap = cap_of(*g), msg = msg_bytes_of(*g);
 
   const size_t lds = sizeof(int32_t) * 4 * (g->D + g->P);
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nc), dim3(256), lds, s, phys_ids, slot_partition,
@@ -459,12 +765,11 @@ int dispatch_impl(const void *x, moe_dtype_t x_dtype, const int32_t *phys_ids,
                      slot_local, status);
   if ((st = launch_status()) != MOE_OK) return st;
 
-  const dim3 grid((unsigned)((g->T + 3) / 4));
   const bool bf16 = x_dtype == MOE_DTYPE_BF16;
   uint8_t *db = (uint8_t *)disp_buf, *rb = (uint8_t *)relay_buf;
   const int nit = (g->H + 1023) / 1024;
 #define MOE_SCATTER(N)                                                                         \
-  launch_scatter<N>(bf16, grid, s, x, phys_ids, slot_partition, slot_local, hist_d, hist_p,     \
+  launch_scatter<N>(bf16, s, x, phys_ids, slot_partition, slot_local, hist_d, hist_p,           \
                     route_rank, slot_count, slot_offset, *g, ct, cps, nc, cap, msg, event_id, db, \
                     rb, slot_rows, disp_row, ret_row, status)
   if (nit <= 1)

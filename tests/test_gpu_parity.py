@@ -27,6 +27,11 @@ RAGGED = mw.Workload("ragged", T=3 * 100, H=384, E=40, P=40, k=8, D=10, Epp=4, S
 FFN_SMALL = mw.Workload("ffn_small", T=2 * 400, H=384, E=32, P=32, k=4, D=8, Epp=4, S=2, LB=400,
                         gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
                         experts="swiglu", combine="bf16", out_dtype="bf16", I=192)
+# decode-size dispatch (at most 1024 routes: one fused launch): three sources,
+# H = 1408 (the second 1024-element slice is partial), skewed routes
+SMALLB = mw.Workload("smallb", T=3 * 40, H=1408, E=24, P=24, k=6, D=12, Epp=2, S=3, LB=40,
+                     gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                     experts="identity", combine="q8", out_dtype="f32")
 # two-hop case: 4 sources, 12 destination partitions, the first 4 are relays
 TWOHOP_SMALL = mw.Workload("twohop_small", T=4 * 40, H=256, E=10, P=12, k=4, D=12, Epp=1, S=4,
                            LB=40, gating="sigmoid", logits_dtype="bf16", x_dtype="bf16",
@@ -334,9 +339,11 @@ def test_pack_expert_weights_image():
 
 # --------------------------------------------------------------- dispatch ---
 
-@pytest.mark.parametrize("name", ["tiny", "decode96", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "decode96", "ragged", "smallb"])
 def test_dispatch_parity_small(name):
-    w = RAGGED if name == "ragged" else mw.WORKLOADS[name]
+    """tiny, decode96 and smallb take the one-launch path for at most 1024 routes,
+    ragged (2400 routes) the count / scan / scatter path."""
+    w = {"ragged": RAGGED, "smallb": SMALLB}.get(name) or mw.WORKLOADS[name]
     c = Case(w)
     _, _, phys = _check_route(c)
     _check_dispatch(c, phys)
@@ -998,6 +1005,92 @@ def test_invalid_routes_are_flagged_not_written():
     dr = host(b.disp_row)
     assert dr[5, 3] == -1 and dr[7, 0] == -1
     assert int(host(b.meta)[..., 2].sum()) == c.w.T * c.w.k - 2
+
+
+def _layout_by_definition(w, phys, sp, event_id):
+    """The dispatch layout written out from its definition (valid routes only,
+    route order t k + j): a route's row in region (d, s) is the number of valid
+    routes before it there (-1 from cap on), its slot row the slot's offset plus
+    the number of valid routes before it to that slot; the status bits flag
+    invalid slots, invalid partitions and full regions."""
+    T, k, P, D, S, LB = w.T, w.k, w.P, w.D, w.S, w.LB
+    cap = LB * min(k, w.Epp)
+    ph = phys.reshape(-1)
+    n = T * k
+    valid = np.zeros(n, bool)
+    d = np.full(n, -1)
+    bits = 0
+    for g in range(n):
+        p = int(ph[g])
+        if not 0 <= p < P:
+            bits |= moe.MOE_DEVICE_BAD_ROUTE
+        elif not 0 <= int(sp[p]) < D:
+            bits |= moe.MOE_DEVICE_BAD_PARTITION
+        else:
+            valid[g], d[g] = True, int(sp[p])
+    src = np.arange(n) // k // LB
+    count_ds = np.zeros((D, S), np.int64)
+    count_p = np.zeros(P, np.int64)
+    rank_d = np.zeros(n, np.int64)
+    rank_p = np.zeros(n, np.int64)
+    for g in np.nonzero(valid)[0]:
+        rank_d[g] = count_ds[d[g], src[g]]
+        rank_p[g] = count_p[ph[g]]
+        count_ds[d[g], src[g]] += 1
+        count_p[ph[g]] += 1
+    if (count_ds > cap).any():
+        bits |= moe.MOE_DEVICE_OVER_CAPACITY
+    slot_offset = np.concatenate([[0], np.cumsum(count_p)]).astype(np.int32)
+    disp_row = np.full(n, -1, np.int32)
+    ret_row = np.full(n, -1, np.int32)
+    slot_rows = np.full(n, -7, np.int32)  # rows no valid route owns are not checked
+    for g in np.nonzero(valid)[0]:
+        r = slot_offset[ph[g]] + rank_p[g]
+        dr = (d[g] * S + src[g]) * cap + rank_d[g] if rank_d[g] < cap else -1
+        disp_row[g], ret_row[g], slot_rows[r] = dr, r, dr
+    meta_off = np.concatenate([np.zeros((D, 1), np.int64), np.cumsum(count_ds, 1)[:, :-1]], 1)
+    return dict(bits=bits, disp_row=disp_row.reshape(T, k), ret_row=ret_row.reshape(T, k),
+                slot_rows=slot_rows, slot_count=count_p.astype(np.int32), slot_offset=slot_offset,
+                meta_off=meta_off, meta_count=count_ds)
+
+
+@pytest.mark.parametrize("name", ["smallb", "ragged"])
+def test_dispatch_layout_with_bad_routes_and_a_full_region(name):
+    """Both dispatch paths (smallb: the one-launch path; ragged: count / scan /
+    scatter) against the layout's definition when the routes are not clean:
+    out-of-range slot ids, a slot whose partition is out of range, and one
+    source sending every route to partition 0 so that region (0, 0) overflows;
+    status bits, row indices, slot counts and offsets, and meta are compared."""
+    w = SMALLB if name == "smallb" else RAGGED
+    c = Case(w)
+    c.layer.route(c.lg_d)
+    b = c.layer.buf
+    sp = c.sp.copy()
+    bad_slot = w.P - 1
+    sp[bad_slot] = w.D + 5
+    c.layer.slot_partition.copy_(to_dev(sp))
+    phys = host(b.phys).copy()
+    phys[:w.LB] = np.arange(w.k)[None, :] % w.Epp  # source 0: every route to partition 0
+    phys[w.LB + 2, 3] = 10_000
+    phys[w.LB + 3, 0] = -3
+    phys[w.LB + 4, 1] = bad_slot
+    b.phys.copy_(to_dev(phys.astype(np.int32)))
+    c.layer.event_id = 76  # the layer advances it: this dispatch carries 77
+    c.layer.dispatch(c.x_d)
+    torch.cuda.synchronize()
+    ref = _layout_by_definition(w, phys, sp, 77)
+    assert b.device_status() == ref["bits"] == (moe.MOE_DEVICE_BAD_ROUTE | moe.MOE_DEVICE_BAD_PARTITION
+                                                | moe.MOE_DEVICE_OVER_CAPACITY)
+    assert np.array_equal(host(b.disp_row), ref["disp_row"]), "disp_row"
+    assert np.array_equal(host(b.ret_row), ref["ret_row"]), "ret_row"
+    sr = host(b.slot_rows)
+    own = ref["slot_rows"] != -7
+    assert np.array_equal(sr[own], ref["slot_rows"][own]), "slot_rows"
+    assert np.array_equal(host(b.slot_count), ref["slot_count"])
+    assert np.array_equal(host(b.slot_offset), ref["slot_offset"])
+    meta = host(b.meta)
+    assert np.all(meta[..., 0].view(np.uint32) == 77)
+    assert np.array_equal(meta[..., 1], ref["meta_off"]) and np.array_equal(meta[..., 2], ref["meta_count"])
 
 
 def test_all_tokens_to_one_partition():
