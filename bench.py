@@ -375,10 +375,14 @@ def time_twohop46080(reps):
 
 def attainable(w, reps=5):
     """Attainable rates on this GPU, for context next to the published peaks: a
-    plain 1 GiB device copy (HBM) and the vendor library's dense INT8 GEMM
-    (torch._int_mm) with the gate/up projection's total ops, i.e. all T*k rows
-    against one expert's [2I][H] weights (one B matrix, full reuse)."""
+    plain 1 GiB device copy (HBM); the int8 matrix-core rate with nothing but
+    MFMAs in flight (moe_probe_mfma_i8: 8 workgroups of 4 wavefronts per CU, each
+    wavefront four independent chains of v_mfma_i32_32x32x32_i8, about as long as
+    the gate/up launch); and the vendor library's dense INT8 GEMM (torch._int_mm)
+    with the gate/up projection's total ops, i.e. all T*k rows against one
+    expert's [2I][H] weights (one B matrix, full reuse)."""
     import torch
+    import combine_moe_route_topk_amd as moe
     out = {}
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
@@ -405,6 +409,14 @@ def attainable(w, reps=5):
     ms = best(lambda: src.sum())
     out["read_GBps"] = round(COPY_BYTES / (ms * 1e-3) / 1e9, 1)
     del src, dst
+    blocks, iters = 8 * 256, 4096
+    probe = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    ms = best(lambda: moe.moe_probe_mfma_i8(blocks, iters, probe))
+    mfma_ops = blocks * 4 * iters * 4 * 2 * 32 * 32 * 32
+    out["mfma_i8_TOPS"] = round(mfma_ops / (ms * 1e-3) / 1e12, 1)
+    out["mfma_i8"] = (f"moe_probe_mfma_i8: {blocks} workgroups x 4 wavefronts x {4 * iters} "
+                      f"v_mfma_i32_32x32x32_i8, {ms:.3f} ms")
+    del probe
     M, K, N = w.T * w.k, w.H, 2 * w.I
     try:
         a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
@@ -699,9 +711,10 @@ def main():
     else:
         del packed
     if not args.no_attainable:
-        log("[bench] attainable rates: device copy, library INT8 GEMM")
+        log("[bench] attainable rates: device copy, MFMA-only int8 rate, library INT8 GEMM")
         att = attainable(w)
         result["attainable"] = att
+        result["roofline"]["frac_of_mfma_attainable"] = round(gu_tops / att["mfma_i8_TOPS"], 4)
         if att.get("int8_gemm_TOPS"):
             result["roofline"]["frac_of_attainable"] = round(gu_tops / att["int8_gemm_TOPS"], 4)
         result["dispatch_combine"]["frac_of_copy"] = round(dc_gbs / att["copy_GBps"], 4)

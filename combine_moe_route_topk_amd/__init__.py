@@ -39,7 +39,8 @@ EXPORTED = ("moe_plan_sizes", "moe_eplb_build_map", "moe_route_topk", "moe_dispa
             "moe_expert_ffn_q8", "moe_expert_gateup_q8", "moe_expert_down_q8",
             "moe_expert_down_q8_int8ret", "moe_relay_returns", "moe_combine", "moe_router_logits",
             "moe_pack_expert_weights", "moe_router_topk", "moe_quant_returns_q8",
-            "moe_dispatch_q8_static", "moe_check_event", "moe_status_string")
+            "moe_dispatch_q8_static", "moe_check_event", "moe_probe_mfma_i8",
+            "moe_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -107,6 +108,7 @@ def lib():
         L.moe_dispatch_q8_static.argtypes = [_P, _I32, _P, _P, ctypes.c_uint32,
                                              ctypes.POINTER(Geom), _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P]
+        L.moe_probe_mfma_i8.argtypes = [_I32, _I32, _P, _P]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -293,6 +295,10 @@ def moe_quant_returns_q8(ret, slot_offset, g: Geom, ret_q8, stream=None):
 def moe_combine(mode: int, src, row, topk_w, g: Geom, out_dtype: int, out, stream=None):
     _check(lib().moe_combine(mode, _ptr(src), _ptr(row), _ptr(topk_w), ctypes.byref(g), out_dtype,
                              _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_probe_mfma_i8(blocks: int, iters: int, out, stream=None):
+    _check(lib().moe_probe_mfma_i8(blocks, iters, _ptr(out), _stream(stream)), "moe_probe_mfma_i8")
 
 
 from .layer import MoeBuffers, MoeLayer, MoePipeline, PackedExpertWeights  # noqa: E402,F401

@@ -197,8 +197,8 @@ int moe_route_topk(const void *logits, moe_dtype_t logits_dtype, const float *bi
  * "INT8：少搬一些": gating stays in BF16/FP32 while the matmuls go INT8; XDS
  * P038: dispatch and combine follow the gating scores]:
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h]
- * bf16 operands, products and sums in fp32 (MFMA), fp32 logits.  Tiles of 96
- * tokens x 128 experts; when they are too few to fill the GPU, the sum over h
+ * bf16 operands, products and sums in fp32 (MFMA), fp32 logits.  Tiles of 192
+ * tokens x 256 experts; when they are too few to fill the GPU, the sum over h
  * is split into router_splits parts (whole 64-element steps) whose partial
  * sums are added in split order, so the result is the same every run; its
  * error against the exact value is within the fp32 summation bound
@@ -469,6 +469,18 @@ int moe_relay_returns(uint16_t *ret, const int32_t *phys_ids, const int32_t *slo
  */
 int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *row, const float *topk_w,
                 const moe_geom_t *g, moe_dtype_t out_dtype, void *out, void *stream);
+
+/*
+ * moe_probe_mfma_i8 -- measurement support, not a step of the MoE path: the
+ * int8 matrix-core rate the device sustains, the ceiling the expert GEMMs are
+ * measured against beside the published peak (which assumes the top clock).
+ * Launches `blocks` workgroups of 256 threads; every wavefront issues
+ * 4 * iters v_mfma_i32_32x32x32_i8 (32x32x32 = 65536 int8 operations each) on
+ * register operands and writes one checksum per thread:
+ *   out  [blocks * 256] int32, device (caller-owned)
+ * Errors: MOE_ERR_INVALID_ARG (blocks or iters <= 0, NULL out).
+ */
+int moe_probe_mfma_i8(int32_t blocks, int32_t iters, int32_t *out, void *stream);
 
 /* Human-readable name of a status code. */
 const char *moe_status_string(int status);

@@ -263,3 +263,12 @@ def test_check_event_validation_and_status_string():
     assert L.moe_check_event(fake, fake, fake, fake, ctypes.byref(g), 1, None,
                              None) == moe.MOE_ERR_INVALID_ARG
     assert "stale" in moe.status_string(moe.MOE_ERR_STALE)
+
+
+def test_mfma_probe_validation():
+    """The MFMA rate probe refuses empty launches and a NULL output before any launch."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_probe_mfma_i8(0, 8, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_mfma_i8(4, 0, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_mfma_i8(4, 8, None, None) == moe.MOE_ERR_INVALID_ARG
