@@ -991,6 +991,49 @@ def test_dispatch_quantization_special_tokens():
     assert s[3] == 1 and q[3, :3].tolist() == [127, 2, -2]
 
 
+def _bf16_bits(v) -> np.ndarray:
+    """bf16 bit patterns of fp32 values that bf16 represents exactly."""
+    b = np.asarray(v, np.float32).view(np.uint32)
+    assert np.all(b & 0xFFFF == 0), "not a bf16 value"
+    return (b >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("T,H", [(300, 384), (1200, 7168)], ids=["per_route", "per_token"])
+def test_dispatch_quantization_special_bf16_tokens(T, H):
+    """bf16 tokens at the edges of the token-wise INT8 rule, bit-exact against the
+    oracle's IEEE quotients, through both scatter shapes (one wavefront per route
+    at 300 tokens, one per token at 1200): subnormal rows (scale below 2^-100),
+    a row whose scale is exactly 2^-100, the largest finite bf16 amax, exact
+    halves at scale 1 (round half to even), signed zeros beside tiny normals, and
+    rows of random bit patterns over the whole finite range."""
+    w = RAGGED.scaled(name=f"ragged_bf16_{T}x{H}", T=T, H=H, LB=T // 3)
+    c = Case(w)
+    rng = np.random.default_rng(47)
+    x = c.x  # uint16 bf16 bits [T][H]
+    sign = lambda n: (rng.integers(0, 2, n).astype(np.uint16) << 15)
+    x[0] = rng.integers(0, 0x80, H).astype(np.uint16) | sign(H)  # subnormals
+    x[0, 0] = 0x007F
+    # |values| <= 127 * 2^-100 (truncated to bf16), the largest one exactly that
+    x[1] = ((rng.uniform(-1, 1, H) * (127.0 * 2.0 ** -100)).astype(np.float32)
+            .view(np.uint32) >> 16).astype(np.uint16)
+    x[1, 0] = _bf16_bits([127.0 * 2.0 ** -100])[0]
+    x[2] = rng.integers(0, 0x7F80, H).astype(np.uint16) | sign(H)  # every finite magnitude
+    x[2, 0] = 0x7F7F
+    x[3] = _bf16_bits(rng.integers(-127, 127, H).astype(np.float32) + np.float32(0.5))
+    x[3, :4] = _bf16_bits([127.0, 2.5, -2.5, 0.5])
+    x[4] = np.where(rng.random(H) < 0.5, np.uint16(0x8000),
+                    rng.integers(0x0080, 0x0200, H).astype(np.uint16) | sign(H))
+    for r in range(5, 12):
+        x[r] = rng.integers(0, 0x7F80, H).astype(np.uint16) | sign(H)
+    c.x_d = dev_bits(x, True)
+    _, _, phys = _check_route(c)
+    q, s, _ = _check_dispatch(c, phys)
+    f32 = lambda b: (np.asarray(b, np.uint32) << 16).view(np.float32)
+    assert s[0] < np.float32(2.0 ** -100) and s[1] == np.float32(2.0 ** -100)
+    assert s[2] == f32(0x7F7F) / np.float32(127)
+    assert s[3] == 1 and q[3, :4].tolist() == [127, 2, -2, 0]
+
+
 def test_invalid_routes_are_flagged_not_written():
     """Out-of-range physical ids are dropped (row indices -1) and reported in the
     device status word; nothing is written out of bounds."""
