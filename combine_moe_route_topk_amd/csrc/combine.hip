@@ -4,12 +4,13 @@
 //  CMI EP320 FusedCombine (all k contributions present, dequantize, weight by
 //  the gate)]
 //
-// One wavefront per token.  The k row gathers of two element groups are issued
-// together (2k x 16 B per lane in flight), then summed in fp32 in ascending
-// route order with separate multiply and add (no FMA contraction), so the
-// result is the same bits as the plain loop on the CPU.  Every value row is
-// read exactly once, so the gathers are non-temporal loads (measured on the
-// 12288-token layer: 284 us instead of 323 us).
+// One wavefront per pair of 1 KB element groups of a token.  The k row
+// gathers of the two groups are issued together (2k x 16 B per lane in
+// flight), then summed in fp32 in ascending route order with separate
+// multiply and add (no FMA contraction), so the result is the same bits as the
+// plain loop on the CPU.  Every value row is read exactly once, so the gathers
+// are non-temporal loads (measured on the 12288-token layer: 284 us instead of
+// 323 us).
 #include <algorithm>
 
 #include "common.h"
@@ -28,9 +29,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
                                                       const float *__restrict__ topk_w, int T,
                                                       int H, int k, int64_t row_bytes, int cs,
                                                       void *__restrict__ out) {
-  // cs wavefronts per token (cs > 1 only for small batches, to spread them
-  // over the GPU): wavefront part of token t takes element groups part,
-  // part + cs, ...; every output element is computed exactly as with one
+  // cs wavefronts per token: wavefront part of token t takes element groups
+  // part, part + cs, ... (the host makes it one pair of groups); every output
+  // element is computed exactly as with one
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t t = wv / cs;
@@ -152,10 +153,15 @@ extern "C" int moe_combine(moe_ret_mode_t mode, const void *src, const int32_t *
   const int64_t rb = (qb || mode == MOE_RET_Q8_ROWS) ? ret_q8_row_bytes_of(*g)
                      : q8                           ? msg_bytes_of(*g)
                                                     : (int64_t)g->H * 2;
-  // wavefronts per token: one, unless the batch is too small to give ~1024
-  // wavefronts; then up to the number of element groups (pairs of 1 KB loads)
+  // wavefronts per token: one per pair of 1 KB element groups (7 at H = 7168
+  // with bf16 rows, 4 with INT8 rows), at every batch size: more, shorter
+  // wavefronts keep more gathers in flight (12288-token layer: bf16 returns
+  // 286 -> 267 us, token-wise INT8 returns 163 -> 153 us against one wavefront
+  // per token).  Block-scaled INT8 returns measured the same either way and
+  // keep one wavefront per token unless the batch is small.
   const int groups = (int)((g->H + 64 * (q8 ? 16 : 8) * 2 - 1) / (64 * (q8 ? 16 : 8) * 2));
-  const int cs = (int)std::max<int64_t>(1, std::min<int64_t>(groups, (1024 + g->T - 1) / g->T));
+  const int cs = qb ? (int)std::max<int64_t>(1, std::min<int64_t>(groups, (1024 + g->T - 1) / g->T))
+                    : groups;
   const dim3 grid((unsigned)(((int64_t)g->T * cs + 3) / 4));
   hipStream_t s = (hipStream_t)stream;
   const bool obf = out_dtype == MOE_DTYPE_BF16;
