@@ -40,6 +40,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 256, BK = 64;
+static_assert(BM == kFfnTileRows, "the scratch's m-tile table assumes 128-row tiles");
 #define MOE_LDS __attribute__((address_space(3)))
 constexpr int LDS_STRIDE = BK;  // bytes per LDS row
 // LDS layout: 16-byte chunk c of tile row r sits at r * BK + 16 * (c ^ ((r >> 2) & 3)).
@@ -67,8 +68,15 @@ constexpr int kXcds = 8;
 enum Mode { GATEUP = 0, DOWN = 1 };
 
 // ------------------------------------------------------------------ prep ---
+// tiles [P + 1]: exclusive prefix of the per-slot m-tile counts, then the
+// total; slot_of [bound]: the slot of each m-tile, so that a GEMM block finds
+// its slot with one load instead of a search over the prefix (slot counts
+// from a dispatch of the same geometry never exceed the bound; m-tiles past it
+// are neither listed nor run).
 __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restrict__ slot_count,
-                                                        int P, int32_t *__restrict__ tiles) {
+                                                        int P, int64_t bound,
+                                                        int32_t *__restrict__ tiles,
+                                                        int32_t *__restrict__ slot_of) {
   __shared__ int sh[16];
   const int p = threadIdx.x, lane = p & 63, wave = p >> 6;
   const int v = p < P ? (slot_count[p] + BM - 1) / BM : 0;
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restric
   for (int w = 0; w < wave; ++w) incl += sh[w];
   if (p < P) tiles[p] = incl - v;
   if (p == P - 1) tiles[P] = incl;
+  for (int64_t u = incl - v; u < incl && u < bound; ++u) slot_of[u] = p;
 }
 
 // ---------------------------------------------------------- tile decode ---
@@ -90,27 +99,24 @@ struct Tile {
   int p, m, n;
   int gsz;  // m-tiles in this tile's group: the blocks that read the same weight n-tile
 };
-// Returns false when this block has no work.  GM: m-tiles per group.
+// Returns false when this block has no work.  GM: m-tiles per group.  Three
+// dependent loads: the total, the slot of the block's m-tile (slot p covers
+// list positions [tiles[p] NT, tiles[p + 1] NT)), then that slot's fields.
 template <int GM>
-__device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t *slot_count,
-                                            int P, int NT, Tile &tl) {
+__device__ __forceinline__ bool decode_tile(const int32_t *tiles, const int32_t *slot_of,
+                                            int64_t bound, const int32_t *slot_count, int P,
+                                            int NT, Tile &tl) {
   const int64_t total = (int64_t)tiles[P] * NT;
   const int64_t per = (total + kXcds - 1) / kXcds;
   const int64_t w = blockIdx.x;
   const int64_t i = w / kXcds;
   if (i >= per) return false;
   const int64_t L = (w % kXcds) * per + i;
-  if (L >= total) return false;
-  // slot: largest p with tiles[p] * NT <= L
-  int lo = 0, hi = P - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)tiles[mid] * NT <= L) lo = mid;
-    else hi = mid - 1;
-  }
-  const int p = lo;
+  if (L >= total || L / NT >= bound) return false;
+  const int p = slot_of[L / NT];
+  const int64_t first = (int64_t)tiles[p] * NT;
   const int mt = (slot_count[p] + BM - 1) / BM;
-  const int64_t local = L - (int64_t)tiles[p] * NT;
+  const int64_t local = L - first;
   const int g = (int)(local / ((int64_t)GM * NT));
   const int rem = (int)(local % ((int64_t)GM * NT));
   const int gsz = min(GM, mt - g * GM);
@@ -147,11 +153,11 @@ __device__ __forceinline__ v4i ds_read16(uint32_t addr) {
 // columns (the n-tile) instead of bf16 -- see the epilogue.
 template <int MODE, bool DBG, bool Q8OUT = false>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
-    const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_count,
-    const int32_t *__restrict__ slot_offset, const int32_t *__restrict__ slot_logical,
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ slot_count, const int32_t *__restrict__ slot_offset, const int32_t *__restrict__ slot_logical,
     const int32_t *__restrict__ slot_rows, const uint8_t *__restrict__ disp_buf, int64_t msg,
     const int8_t *__restrict__ hq, const float *__restrict__ hs, const int8_t *__restrict__ w,
-    const float *__restrict__ wscale, int P, int E, int H, int I, int64_t nrows,
+    const float *__restrict__ wscale, int P, int E, int H, int I, int64_t nrows, int64_t mt_bound,
     float *__restrict__ h_out, float *__restrict__ pmax, uint16_t *__restrict__ ret,
     int64_t ret_row_bytes, int32_t *__restrict__ acc_dbg) {
   constexpr int MB = BM / 32, NB = 2;       // MFMA blocks per wave
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   const int K = MODE == GATEUP ? H : I;
   const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
   Tile tl;
-  if (!decode_tile<kGroupM<MODE>>(tiles, slot_count, P, NT, tl)) return;
+  if (!decode_tile<kGroupM<MODE>>(tiles, slot_of, mt_bound, slot_count, P, NT, tl)) return;
   const int e = slot_logical[tl.p];
   if (e < 0 || e >= E) return;
   const int cnt = slot_count[tl.p];
@@ -172,9 +178,11 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // per-row scale of this tile (activation scale s_x, or hs)
+  // per-row scale of this tile (activation scale s_x, or hs): loaded now,
+  // stored to LDS only after the main loop, so that waiting for it does not
+  // hold back the loop's first loads
+  float sc = 0.0f;
   if (tid < BM) {
-    float sc = 0.0f;
     const int64_t rr = row0 + tid;
     if (tid < rows_here && rr < nrows) {
       if (MODE == GATEUP) {
@@ -184,7 +192,6 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         sc = hs[rr];
       }
     }
-    row_scale[tid] = sc;
   }
 
   // Global -> LDS by DMA (global_load_lds_dwordx4): each wavefront instruction
@@ -350,6 +357,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     if (tl.gsz == 1) run(Yes{});
     else run(No{});
   }
+  if (tid < BM) row_scale[tid] = sc;
   __syncthreads();
 
 
@@ -660,7 +668,7 @@ namespace {
 
 struct FfnArgs {
   FfnScratch L;
-  int32_t *tiles;
+  int32_t *tiles, *slot_of;
   float *pmax, *h, *hs;
   int8_t *hq;
   int64_t nrows, msg, mt_bound;
@@ -676,13 +684,14 @@ int ffn_common(const moe_geom_t *g, int32_t I, void *scratch, size_t scratch_byt
   uint8_t *sc = (uint8_t *)scratch;
   *a = FfnArgs{L,
                   (int32_t *)(sc + L.tiles),
+                  (int32_t *)(sc + L.slot_of),
                   (float *)(sc + L.pmax),
                   (float *)(sc + L.h),
                   (float *)(sc + L.hs),
                   (int8_t *)(sc + L.hq),
                   (int64_t)g->T * g->k,
                   msg_bytes_of(*g),
-                  (int64_t)g->T * g->k / BM + g->P};
+                  ffn_mtile_bound(*g)};
   return MOE_OK;
 }
 
@@ -713,15 +722,16 @@ extern "C" int moe_expert_gateup_q8(const void *disp_buf, const int32_t *slot_co
   if (!aligned16(disp_buf) || !aligned16(w_gateup) || !aligned16(s_gateup))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->tiles);
+  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(1024), 0, s, slot_count, g->P, a->mt_bound,
+                     a->tiles, a->slot_of);
   if ((st = launch_status()) != MOE_OK) return st;
   const dim3 grid = gemm_grid(a->mt_bound, (I + BN / 2 - 1) / (BN / 2));
 #define MOE_GATEUP(DBG)                                                                         \
-  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP, DBG>), grid, dim3(256), 0, s, a->tiles, slot_count, \
-                     slot_offset, slot_logical, slot_rows, (const uint8_t *)disp_buf, a->msg,      \
-                     (const int8_t *)nullptr, (const float *)nullptr, w_gateup, s_gateup, g->P,    \
-                     g->E, g->H, I, a->nrows, a->h, a->pmax, (uint16_t *)nullptr, (int64_t)0,      \
-                     acc_gateup_dbg)
+  hipLaunchKernelGGL((ffn_gemm_kernel<GATEUP, DBG>), grid, dim3(256), 0, s, a->tiles,         \
+                     a->slot_of, slot_count, slot_offset, slot_logical, slot_rows,              \
+                     (const uint8_t *)disp_buf, a->msg, (const int8_t *)nullptr,                \
+                     (const float *)nullptr, w_gateup, s_gateup, g->P, g->E, g->H, I, a->nrows, \
+                     a->mt_bound, a->h, a->pmax, (uint16_t *)nullptr, (int64_t)0, acc_gateup_dbg)
   if (acc_gateup_dbg)
     MOE_GATEUP(true);
   else
@@ -754,10 +764,11 @@ int expert_down(const int32_t *slot_count, const int32_t *slot_offset,
   const dim3 grid = gemm_grid(a->mt_bound, (g->H + BN - 1) / BN);
   const int64_t rb = q8out ? ret_q8_row_bytes_of(*g) : (int64_t)g->H * 2;
 #define MOE_DOWN(DBG, Q)                                                                        \
-  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN, DBG, Q>), grid, dim3(256), 0, s, a->tiles, slot_count, \
-                     slot_offset, slot_logical, (const int32_t *)nullptr, (const uint8_t *)nullptr, \
-                     a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E, g->H, I, a->nrows,          \
-                     (float *)nullptr, (float *)nullptr, (uint16_t *)ret, rb, acc_down_dbg)
+  hipLaunchKernelGGL((ffn_gemm_kernel<DOWN, DBG, Q>), grid, dim3(256), 0, s, a->tiles,         \
+                     a->slot_of, slot_count, slot_offset, slot_logical, (const int32_t *)nullptr, \
+                     (const uint8_t *)nullptr, a->msg, a->hq, a->hs, w_down, s_down, g->P, g->E,  \
+                     g->H, I, a->nrows, a->mt_bound, (float *)nullptr, (float *)nullptr,          \
+                     (uint16_t *)ret, rb, acc_down_dbg)
   if (q8out) {
     if (acc_down_dbg) MOE_DOWN(true, true);
     else MOE_DOWN(false, true);

@@ -55,6 +55,8 @@ FfnScratch ffn_scratch_layout(const moe_geom_t &g, int32_t I) {
   int64_t o = 0;
   L.tiles = o;
   o = up256(o + 4 * ((int64_t)g.P + 2));
+  L.slot_of = o;
+  o = up256(o + 4 * ffn_mtile_bound(g));
   L.pmax = o;
   o = up256(o + 4 * rows * (I / 64));
   L.h = o;

@@ -40,6 +40,13 @@ inline int64_t ret_q8_row_bytes_of(const moe_geom_t &g) {
   return ((int64_t)g.H + 4 * nblk + 127) / 128 * 128;
 }
 
+// Rows of an expert-GEMM m-tile; a slot of n rows has ceil(n / 128) m-tiles,
+// so T k routes make at most T k / 128 + P of them.
+constexpr int kFfnTileRows = 128;
+inline int64_t ffn_mtile_bound(const moe_geom_t &g) {
+  return (int64_t)g.T * g.k / kFfnTileRows + g.P;
+}
+
 // Image of the INT8 expert weights (moe_pack_expert_weights): one 16 KB block
 // per (expert, n-tile, 64-byte K step), n-tiles of 128 gate/up pairs
 // (gate/up) or 256 output channels (down), K padded to whole groups of four
@@ -82,6 +89,7 @@ DispatchScratch dispatch_scratch_layout(const moe_geom_t &g);
 // Byte layout of the expert-FFN scratch.
 struct FfnScratch {
   int64_t tiles;     // int32 [P + 1]: exclusive prefix of per-slot m-tile counts, then the total
+  int64_t slot_of;   // int32 [T*k/128 + P]: the slot of each m-tile (slot-major order)
   int64_t pmax;      // fp32 [T*k][I/64]  max |h| of each row over each gate-up n-tile
   int64_t h;         // fp32 [T*k][I]
   int64_t hq;        // int8 [T*k][I]
