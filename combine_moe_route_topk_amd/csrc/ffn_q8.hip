@@ -78,6 +78,7 @@ __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restric
                                                         int32_t *__restrict__ tiles,
                                                         int32_t *__restrict__ slot_of) {
   __shared__ int sh[16];
+  __shared__ int start[MOE_MAX_P + 1];
   const int p = threadIdx.x, lane = p & 63, wave = p >> 6;
   const int v = p < P ? (slot_count[p] + BM - 1) / BM : 0;
   int incl = v;
@@ -89,9 +90,27 @@ __global__ __launch_bounds__(1024) void ffn_prep_kernel(const int32_t *__restric
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
   for (int w = 0; w < wave; ++w) incl += sh[w];
-  if (p < P) tiles[p] = incl - v;
-  if (p == P - 1) tiles[P] = incl;
-  for (int64_t u = incl - v; u < incl && u < bound; ++u) slot_of[u] = p;
+  if (p < P) {
+    tiles[p] = incl - v;
+    start[p] = incl - v;
+  }
+  if (p == P - 1) {
+    tiles[P] = incl;
+    start[P] = incl;
+  }
+  __syncthreads();
+  // m-tile u belongs to the largest slot q with start[q] <= u (empty slots
+  // share their start with the next one and are skipped that way)
+  const int64_t total = start[P] < bound ? start[P] : bound;
+  for (int64_t u = p; u < total; u += blockDim.x) {
+    int lo = 0, hi = P - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= u) lo = mid;
+      else hi = mid - 1;
+    }
+    slot_of[u] = lo;
+  }
 }
 
 // ---------------------------------------------------------- tile decode ---
