@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t *__restrict_
         uint32_t pk[EPL / 2];
 #pragma unroll
         for (int e = 0; e < EPL / 2; ++e)
-          pk[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+          pk[e] = bf16x2_bits(acc[2 * e], acc[2 * e + 1]);
         uint4 *dst = (uint4 *)((uint16_t *)out + t * H + e0);
 #pragma unroll
         for (int q = 0; q < EPL / 8; ++q)

@@ -26,13 +26,16 @@ inline int launch_status() { return hip_status(hipGetLastError()); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
-// round to nearest even (finite inputs; infinities stay infinite, NaN is kept
-// a NaN); written without branches so that it vectorizes in epilogues
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t special = (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  return (u & 0x7f800000u) == 0x7f800000u ? special : rounded;
+// Two fp32 values -> packed bf16 bits (lo in the low half), round to nearest
+// even, by one v_cvt_pk_bf16_f32.  For every non-NaN fp32 input this gives the
+// bits of the textbook rounding (u + 0x7fff + ((u >> 16) & 1)) >> 16, finite
+// values that round past the largest bf16 becoming infinities (all 2^32
+// inputs compared on the device); NaN inputs come out as quiet NaNs.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 r = __builtin_convertvector((f2){lo, hi}, b2);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {

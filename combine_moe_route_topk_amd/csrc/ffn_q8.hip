@@ -184,6 +184,9 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   // output staging of the epilogue
   __shared__ __attribute__((aligned(16))) uint8_t lds[kArena];
   __shared__ float row_scale[BM];
+  // the tile's column scales (GATEUP: 128 gate, then the 128 matching up;
+  // DOWN: 256 output channels), fetched by one DMA before the main loop
+  __shared__ __attribute__((aligned(16))) float col_scale[BN];
 
   const int K = MODE == GATEUP ? H : I;
   const int NT = MODE == GATEUP ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;
@@ -211,6 +214,21 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         sc = hs[rr];
       }
     }
+  }
+
+  // Column scales: one wave instruction of 16 bytes per lane into col_scale
+  // (lane l -> floats 4l .. 4l + 3), issued before every load of the main
+  // loop, so the loop's first wait covers it.  Addresses past the row are
+  // clamped to its last run; the epilogue zeroes those columns.
+  if (wave == 0) {
+    const float *src;
+    if (MODE == GATEUP) {
+      const int n = min(tl.n * (BN / 2) + 4 * (lane & 31), I - 4);
+      src = wscale + (int64_t)e * 2 * I + (lane >> 5) * I + n;
+    } else {
+      src = wscale + (int64_t)e * H + min(tl.n * BN + 4 * lane, H - 4);
+    }
+    __builtin_amdgcn_global_load_lds(src, (MOE_LDS void *)col_scale, 16, 0, 0);
   }
 
   // Global -> LDS by DMA (global_load_lds_dwordx4): each wavefront instruction
@@ -398,9 +416,9 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int n = nw + 8 * g4;  // I % 64 == 0: a run is all below I or all past it
-      const float4 a = n < I ? *(const float4 *)(wscale + (int64_t)e * 2 * I + n)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 b = n < I ? *(const float4 *)(wscale + (int64_t)e * 2 * I + I + n)
+      const int ln = wave * 32 + 4 * half + 8 * g4;  // the run's pair index in the tile
+      const float4 a = n < I ? *(const float4 *)(col_scale + ln) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = n < I ? *(const float4 *)(col_scale + BN / 2 + ln)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
       sgv[g4][0] = a.x; sgv[g4][1] = a.y; sgv[g4][2] = a.z; sgv[g4][3] = a.w;
       suv[g4][0] = b.x; suv[g4][1] = b.y; suv[g4][2] = b.z; suv[g4][3] = b.w;
@@ -474,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int c = n0 + sb + 8 * g4;  // H % 128 == 0: a run is all below H or all past it
-        const float4 v = c < H ? *(const float4 *)(wscale + (int64_t)e * H + c)
+        const float4 v = c < H ? *(const float4 *)(col_scale + sb + 8 * g4)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
         sdv[g4][0] = v.x; sdv[g4][1] = v.y; sdv[g4][2] = v.z; sdv[g4][3] = v.w;
       }
@@ -485,16 +503,16 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
         const float hsr = row_scale[lr];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          uint32_t b[4];
+          float y[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int32_t a = acc[mb][nb][4 * g4 + q];
-            b[q] = f32_to_bf16_bits(((float)a * hsr) * sdv[g4][q]);
+            y[q] = ((float)a * hsr) * sdv[g4][q];
             const int c = n0 + sb + 8 * g4 + q;
             if (DBG && lr < rows_here && rr < nrows && c < H) acc_dbg[rr * H + c] = a;
           }
           *(uint2 *)(stb + lr * (kStageStrideB / 2) + sb + 8 * g4) =
-              make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+              make_uint2(bf16x2_bits(y[0], y[1]), bf16x2_bits(y[2], y[3]));
         }
       }
     }

@@ -610,6 +610,45 @@ def test_combine_bf16_returns_global12288():
                  "combine end to end")
 
 
+def test_combine_bf16_output_rounding_edges():
+    """The bf16 output's round to nearest even, bit-exact against the oracle, where
+    it is hardest: each token's sum is one fp32 product w * v (the second route
+    weighs 0), over random values of every exponent, subnormal products, exact
+    ties (even and odd neighbours) and the bf16 maximum times (1 + 2^-9) and
+    (1 + 2^-8), which round to the maximum and to infinity."""
+    T, k, H = 64, 2, 1024
+    g = moe.geom(T=T, H=H, E=8, P=8, k=k, D=8, Epp=1, S=1, LB=T)
+    rng = np.random.default_rng(53)
+    rets = np.zeros((T * k, H), np.uint16)
+    w = np.zeros((T, k), np.float32)
+    # random finite bf16 values up to 2^119 and weights 2^-40 .. 2^7: products stay finite
+    exp_bits = rng.integers(0, 0xF7, (T, H)).astype(np.uint16)
+    rets[0::k] = (rng.integers(0, 2, (T, H)).astype(np.uint16) << 15) | (exp_bits << 7) | \
+        rng.integers(0, 0x80, (T, H)).astype(np.uint16)
+    rets[1::k] = rng.integers(0, 0x7F00, (T, H)).astype(np.uint16)
+    w[:, 0] = (rng.uniform(1, 2, T) * np.exp2(rng.integers(-40, 8, T)) *
+               rng.choice([-1, 1], T)).astype(np.float32)
+    w[0, 0] = np.float32(2.0 ** -15)  # token 0: products of tiny values are fp32 subnormals
+    rets[0] = (rng.integers(0x0080, 0x0A00, H)).astype(np.uint16)
+    f2b = lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w[1, 0] = np.float32(1 + 2.0 ** -8)  # token 1: ties between bf16 neighbours
+    rets[2, :4] = f2b([1.0, 1.0078125, -1.0, -1.0078125])
+    w[2, 0] = np.float32(1 + 2.0 ** -9)  # tokens 2, 3: the bf16 maximum, rounded down / up
+    w[3, 0] = np.float32(1 + 2.0 ** -8)
+    rets[4, :] = 0x7F7F
+    rets[6, :] = 0x7F7F
+    ret_d = torch.from_numpy(rets.view(np.int16)).cuda()
+    row = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(moe.RET_BF16, ret_d, to_dev(row), to_dev(w), g, moe.DTYPE_BF16, out)
+    ref = oracle.combine(rets, row, w, k, H, "bf16", True)
+    got = host(out.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got, ref), "bf16 output bits"
+    assert got[1, 0] == 0x3F80 and got[1, 1] == 0x3F82  # ties go to the even neighbour
+    assert np.all(got[2] == 0x7F7F) and np.all(got[3] == 0x7F80)
+    assert np.any((got[0] & 0x7F80) == 0) and np.any(got[0] & 0x7FFF)  # subnormal outputs
+
+
 def test_combine_twohop_returns_equal_direct():
     """E2A through relays gives the same bf16 output bits as reading the returns directly."""
     c = Case(TWOHOP_SMALL)
