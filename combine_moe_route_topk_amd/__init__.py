@@ -23,6 +23,8 @@ MOE_ERR_STALE = -4
 MOE_ERR_HIP = -5
 
 MOE_STATIC_SCRATCH_BYTES = 16 << 20  # the allocation-free dispatch's scratch per GPU
+# the header's limits (MOE_MAX_E, MOE_MAX_P, MOE_MAX_D, MOE_MAX_K, MOE_MAX_H)
+MAX_E, MAX_P, MAX_D, MAX_K, MAX_H = 1024, 1024, 1024, 16, 16384
 
 MOE_DEVICE_BAD_ROUTE = 1
 MOE_DEVICE_BAD_PARTITION = 2

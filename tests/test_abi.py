@@ -34,6 +34,28 @@ def test_library_exports_every_declared_symbol():
     assert moe.status_string(moe.MOE_ERR_CAPACITY) == "capacity exceeded"
 
 
+def test_limits_match_the_header_and_bound_the_geometry():
+    """The binding's limits are the header's #defines, and the host validation
+    takes each limit and refuses one past it."""
+    txt = open(os.path.join(ROOT, "include", "moe_route_topk.h")).read()
+    for name in ("E", "P", "D", "K", "H"):
+        m = re.search(r"#define MOE_MAX_%s (\d+)" % name, txt)
+        assert m and int(m.group(1)) == getattr(moe, "MAX_" + name), name
+    ok = dict(T=64, H=moe.MAX_H, E=moe.MAX_E, P=moe.MAX_P, k=moe.MAX_K, D=moe.MAX_D, Epp=1, S=1,
+              LB=64)
+    assert moe.moe_plan_sizes(moe.geom(**ok), 2048).cap_rows == 64
+    for key, bad in (("H", moe.MAX_H + 16), ("k", moe.MAX_K + 1)):
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_plan_sizes(moe.geom(**dict(ok, **{key: bad})), 2048)
+        assert e.value.status == moe.MOE_ERR_UNSUPPORTED, key
+    for key in ("E", "P", "D"):
+        big = dict(ok, E=moe.MAX_E + 1, P=moe.MAX_P + 1, D=moe.MAX_D + 1)
+        big = dict(ok, **{k: v for k, v in big.items() if k in ("P", key)})
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_plan_sizes(moe.geom(**big), 2048)
+        assert e.value.status == moe.MOE_ERR_UNSUPPORTED, key
+
+
 def test_plan_sizes_reproduce_printed_static_buffers():
     """CMI 缓冲区公式: 320 ranks, local batch 96, 1 expert per die, top-8 ->
     225 MiB dispatch (7680-byte messages) and 420 MiB bf16 combine per die."""

@@ -584,6 +584,38 @@ def test_combine_q8_identity_experts(name):
     assert np.all(np.abs(host(out2) - xf) <= s[:, None] * 0.5 + 1e-5 * np.abs(xf) + 1e-6)
 
 
+# the ABI's limits: H = MOE_MAX_H (the scatter's sixteen 1024-element slices per
+# row), k = MOE_MAX_K, E = P = D = 1024 (the top-k's sixteen experts per lane);
+# 3072 routes take the count / scan / scatter path, 1024 the one-launch path
+MAXDIM = mw.Workload("maxdim", T=2 * 96, H=16384, E=1024, P=1024, k=16, D=1024, Epp=1, S=2, LB=96,
+                     gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                     experts="identity", combine="q8", out_dtype="f32")
+MAXDIM_SMALL = MAXDIM.scaled(name="maxdim_small", T=64, S=1, LB=64)
+
+
+@pytest.mark.parametrize("w", [MAXDIM, MAXDIM_SMALL], ids=lambda w: w.name)
+def test_dispatch_and_combine_at_the_abi_limits(w):
+    """Route, dispatch and the identity-expert combine at the ABI's maximum
+    H, k, E, P and D: ids, layout and every message row bit-exact, the combine
+    bit-exact given the same fp32 weights and within tolerance end to end."""
+    assert w.H == moe.MAX_H and w.k == moe.MAX_K and w.P == moe.MAX_P and w.D == moe.MAX_D
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    assert (w.T * w.k > 1024) == (w.name == "maxdim"), "both dispatch paths are covered"
+    b = c.layer.buf
+    rows = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    w32 = tw.astype(np.float32)
+    ref = oracle.combine(rows, ident, w32, w.k, w.H, "q8", False, scale_offset=w.H)
+    c.layer.combine("q8")
+    assert_close(host(b.out), ref, FP32_RTOL, FP32_ATOL, "combine end to end")
+    out2 = torch.empty_like(b.out)
+    moe.moe_combine(moe.RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, to_dev(w32), c.g,
+                    moe.DTYPE_F32, out2)
+    assert np.array_equal(host(out2), ref), "combine with identical weights is bit-exact"
+
+
 def test_combine_bf16_returns_global12288():
     """Synthetic bf16 expert returns at T=12288: bf16 output bit-identical to the
     oracle given the same fp32 weights, and within tolerance end to end."""
@@ -692,6 +724,47 @@ def test_expert_ffn_parity_small():
     sc = lay["slot_count"]
     assert sc.max() > 256, "want a slot spanning three 128-row m-tiles"
     assert 0 < sc[sc > 0].min() < 32, "want a slot smaller than one 32-row MFMA block"
+    n = w.T * w.k
+    acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
+    acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
+    c.layer.experts(acc_gu, acc_d)
+    torch.cuda.synchronize()
+    b = c.layer.buf
+    logical = c.sl[phys.ravel()]
+    ret = host(b.ret.view(torch.int16)).view(np.uint16)
+    agu, ad = host(acc_gu), host(acc_d)
+    rr = lay["ret_row"].ravel()
+    for e in np.unique(logical):
+        sel = np.nonzero(logical == e)[0]
+        toks = sel // w.k
+        y, hq, hs, o_gu, o_d = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e],
+                                                 want_acc=True)
+        assert np.array_equal(agu[rr[sel]], o_gu), f"gate/up accumulators, expert {e}"
+        assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
+        assert np.array_equal(ret[rr[sel]], y), f"return rows, expert {e}"
+
+
+# expert GEMMs at the ABI's widths: I = 4096 and I = 16384 (the requantization
+# takes a second pass over rows longer than 2048 values; 32 and 128 gate/up
+# n-tiles), and H = MOE_MAX_H (256 K steps of gate/up, 64 down n-tiles)
+FFN_WIDE = [
+    mw.Workload("ffn_wide_i", T=2 * 200, H=512, E=8, P=8, k=2, D=4, Epp=2, S=2, LB=200,
+                gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                experts="swiglu", combine="bf16", out_dtype="bf16", I=4096),
+    mw.Workload("ffn_max_i", T=100, H=256, E=4, P=4, k=2, D=2, Epp=2, S=1, LB=100,
+                gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                experts="swiglu", combine="bf16", out_dtype="bf16", I=16384),
+    mw.Workload("ffn_max_h", T=160, H=16384, E=4, P=4, k=2, D=2, Epp=2, S=1, LB=160,
+                gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                experts="swiglu", combine="bf16", out_dtype="bf16", I=256),
+]
+
+
+@pytest.mark.parametrize("w", FFN_WIDE, ids=lambda w: w.name)
+def test_expert_ffn_parity_at_the_abi_widths(w):
+    """Both GEMMs' int32 accumulators and the bf16 return rows bit-exact at the
+    widest H and I the ABI takes."""
+    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
     n = w.T * w.k
     acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
     acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
