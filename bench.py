@@ -567,6 +567,10 @@ def main():
     ap.add_argument("--router-only", action="store_true",
                     help="time only the gate logits (moe_router_logits, moe_router_topk) on "
                          "the workload's hidden states: every gate launch then has that shape")
+    ap.add_argument("--config-only", choices=("layer12288_uniform", "eplb4096", "decode96",
+                                              "twohop46080"),
+                    help="time only this workload's line of the configs (for profiling runs: "
+                         "every launch then belongs to it); prints {workload, config}")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
@@ -585,6 +589,22 @@ def main():
         copy_calibration()
         return
     w = mw.WORKLOADS[args.workload]
+    if args.config_only:
+        name = args.config_only
+        if name == "decode96":
+            r = time_decode96(200)
+        elif name == "twohop46080":
+            r = time_twohop46080(max(5, args.steps // 5))
+        else:
+            # both take the headline layer's packed expert weights
+            layer, x, lg = build_layer(w)
+            packed = layer.weights
+            del layer, x, lg
+            torch.cuda.empty_cache()
+            r = (time_uniform if name == "layer12288_uniform" else time_eplb4096)(
+                packed, args.steps, args.warmup)
+        print(json.dumps({"workload": name, "config": r}), flush=True)
+        return
     A = algorithmic(w)
     layer, x, lg = build_layer(w)
     if args.router_only:
