@@ -178,6 +178,13 @@ def check_kernel(name: str, lines) -> list:
 KERNELS = r"(ffn_gemm_kernel|router_gemm_kernel)"
 
 
+def inline_loads(lines) -> int:
+    """Instructions of the kinds the check tracks that sit between the
+    compiler's inline-assembly markers."""
+    return sum(1 for t, a in _instructions(lines)
+               if a and t.startswith(("global_load_dwordx4", "ds_read_b128")))
+
+
 def check_asm(path: str, kernel_regex: str = KERNELS) -> list:
     lines = open(path).read().splitlines()
     starts = [i for i, l in enumerate(lines)
@@ -187,9 +194,16 @@ def check_asm(path: str, kernel_regex: str = KERNELS) -> list:
         end = next((j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end")),
                    len(lines))
         body = lines[i:end + 1]
+        name = lines[i].split(":")[0]
         if any("global_load_dwordx4" in l or "ds_read_b128" in l for l in body):
             checked += 1
-        bad += check_kernel(lines[i].split(":")[0], body)
+            # the kernels issue these loads only from inline assembly: if none is
+            # recognised as such (the compiler's markers changed, say), the
+            # analysis below would pass without having tracked anything
+            if inline_loads(body) == 0:
+                bad.append(f"{name}: no inline-assembly load recognised; the listing's "
+                           "format is not the one this check reads")
+        bad += check_kernel(name, body)
     if checked == 0:
         bad.append(f"{path}: no kernel with inline-assembly loads was found")
     return bad

@@ -6,7 +6,7 @@ register, a path that skips the consumer or the wait, a load still pending at
 the end), and accept a vmcnt(0) drain."""
 import pytest
 
-from combine_moe_route_topk_amd.isa_check import check_kernel
+from combine_moe_route_topk_amd.isa_check import check_asm, check_kernel
 
 LOAD = [";;#ASMSTART", "global_load_dwordx4 v[10:13], v[2:3], off", ";;#ASMEND"]
 MFMA = ["v_mfma_i32_32x32x32_i8 v[20:35], v[40:43], v[10:13], v[20:35]"]
@@ -109,3 +109,18 @@ def test_the_built_kernels_have_loads_to_check(src, loads, reads, tmp_path):
     assert text.count("global_load_dwordx4") >= loads
     assert text.count("ds_read_b128") >= reads
     assert check_asm(asm) == []
+
+
+def test_listing_without_inline_markers_is_refused(tmp_path):
+    """A kernel whose loads the check cannot see as inline assembly (no
+    ;;#ASMSTART markers) must fail, not pass without tracking anything; the same
+    kernel with the markers passes."""
+    name = "_Z15ffn_gemm_kernelv"
+    def listing(body):
+        p = tmp_path / "k.s"
+        p.write_text("\n".join([f"{name}:"] + body + [".Lfunc_end0:"]) + "\n")
+        return str(p)
+    plain = [l for l in LOAD if not l.startswith(";;#")]
+    assert check_asm(listing(plain + MFMA + END))
+    assert check_asm(listing(LOAD + MFMA + END)) == []
+
