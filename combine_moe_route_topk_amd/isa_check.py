@@ -5,28 +5,35 @@ and read their LDS fragments with inline-assembly ``ds_read_b128``; the
 compiler tracks neither (its wait-count pass cannot follow a register ring
 across the loop edge, and would order a tracked LDS read after every DMA in
 flight).  They are correct only if the generated code never touches a load's
-destination registers before the data has landed.  For a weight load the
-kernel's own waits guarantee landing at the MFMA that consumes the buffer; for
-an LDS read, at the kernel's explicit ``lgkmcnt(0)``.  This module compiles the
-kernels to assembly and runs a dataflow analysis over each kernel's
-control-flow graph, with the set of pending registers (loading, not yet
-consumed or waited for) as the state:
+destination registers before the data has landed: a weight load lands at an
+``s_waitcnt vmcnt(N)`` issued after at least N later vector-memory instructions
+(vector memory operations complete in issue order), an LDS read at an
+``s_waitcnt`` with ``lgkmcnt(0)``.  This module compiles the kernels to assembly
+and runs a dataflow analysis over each kernel's control-flow graph, with the
+pending registers (loading, not yet landed) as the state -- for a weight load,
+with the number of vector-memory instructions issued after it:
 
   * an inline-assembly ``global_load_dwordx4`` or ``ds_read_b128`` adds its
     destination registers (they must not be pending already, nor its address
     registers);
-  * a ``v_mfma`` reading pending weight-load registers as sources consumes
-    them (its destination must not be pending, and none of its sources may be
-    a pending LDS read);
-  * ``s_waitcnt vmcnt(0)`` clears the pending weight loads, an ``s_waitcnt``
-    with ``lgkmcnt(0)`` the pending LDS reads;
-  * any other instruction that reads or writes a pending register is a
-    violation (a copy or a spill would take the value before it lands), and so
-    is a pending register at ``s_endpgm``;
-  * at control-flow joins the sets are united, iterated to a fixed point.
+  * every vector-memory instruction (``global_``, ``buffer_``, ``flat_``,
+    ``scratch_``: loads, stores, the DMA into LDS) counts one more for each
+    pending weight load;
+  * ``s_waitcnt vmcnt(N)`` lands the weight loads with at least N instructions
+    after them, an ``s_waitcnt`` with ``lgkmcnt(0)`` the LDS reads;
+  * any instruction that reads or writes a pending register -- the MFMA that
+    consumes it included -- is a violation (a copy, a spill or an MFMA would
+    take the value before it lands), and so is a pending register at
+    ``s_endpgm``; so the check also proves the kernels' wait counts;
+  * at control-flow joins a register pending on either path is pending, with
+    the smaller count, iterated to a fixed point.
 
 ``check()`` raises on any violation; the library's build calls it, so a build
-whose register allocation breaks the invariant leaves no library.
+whose register allocation or wait counts break the invariant leaves no library.
+Not covered: the A operand's DMA into LDS (a compiler builtin) must also have
+landed before the barrier after which other wavefronts read that stage; the
+check does not follow LDS addresses, so that rests on the same wait counts and
+on the GPU parity tests.
 """
 from __future__ import annotations
 
@@ -99,44 +106,68 @@ def _blocks(ins):
     return blocks, succ
 
 
-def _step(t: str, is_asm: bool, pending: set, bad: list, name: str) -> set:
-    """One instruction's effect on the pending set: ("vm", r) for a register an
+_VMEM = ("global_", "buffer_", "flat_", "scratch_")
+_VMCNT_MAX = 63
+
+
+def _vmcnt(t: str):
+    m = re.search(r"vmcnt\((\d+)\)", t)
+    return int(m.group(1)) if m else None
+
+
+def _step(t: str, is_asm: bool, pending: dict, bad: list, name: str) -> dict:
+    """One instruction's effect on the pending map.  Keys: ("vm", r) for a register an
     untracked global load is filling, ("lds", r) for one an untracked LDS read is
-    filling."""
+    filling; the value of a "vm" key counts the vector-memory instructions issued
+    after that load (they complete in issue order, so s_waitcnt vmcnt(N) has landed
+    every load with at least N issued after it)."""
     if t.endswith(":"):
         return pending
     op, args = _operands(t)
     if op == "s_waitcnt":
-        if "vmcnt(0)" in t:
-            pending = {p for p in pending if p[0] != "vm"}
+        n = _vmcnt(t)
+        if n is not None:
+            pending = {k: c for k, c in pending.items() if k[0] != "vm" or c < n}
         if "lgkmcnt(0)" in t:
-            pending = {p for p in pending if p[0] != "lds"}
+            pending = {k: c for k, c in pending.items() if k[0] != "lds"}
         return pending
     if op == "s_endpgm":
         if pending:
             bad.append(f"{name}: registers {_names(pending)} still loading at s_endpgm")
         return pending
     regs = {r for _, r in pending}
+    if op.startswith(_VMEM):
+        pending = {k: (min(c + 1, _VMCNT_MAX + 1) if k[0] == "vm" else c)
+                   for k, c in pending.items()}
     if is_asm and op in ("global_load_dwordx4", "ds_read_b128"):
         dst, addr = _regs(args[0]), _regs(args[1])
         if (dst | addr) & regs:
             bad.append(f"{name}: '{t}' while {sorted((dst | addr) & regs)[:8]} are still loading")
         kind = "vm" if op.startswith("global") else "lds"
-        return {p for p in pending if p[1] not in dst} | {(kind, r) for r in dst}
+        pending = {k: c for k, c in pending.items() if k[1] not in dst}
+        pending.update({(kind, r): 0 for r in dst})
+        return pending
     touched = _regs(t) & regs
     if not touched:
         return pending
-    hit = {p for p in pending if p[1] in touched}
-    if (op.startswith("v_mfma") and not (_regs(args[0]) & regs)
-            and all(k == "vm" for k, _ in hit)):
-        return pending - hit  # consumed: the kernel's waits make the data land here
-    bad.append(f"{name}: '{t}' touches {_names(hit)} before the load into them is "
-               + ("waited for" if any(k == "lds" for k, _ in hit) else "consumed"))
-    return pending - hit
+    hit = {k for k in pending if k[1] in touched}
+    bad.append(f"{name}: '{t}' touches {_names(hit)} before the load into them "
+               + ("is waited for (lgkmcnt(0))" if any(k == "lds" for k, _ in hit)
+                  else "has landed (no s_waitcnt vmcnt(N) with N loads issued after it)"))
+    return {k: c for k, c in pending.items() if k not in hit}
 
 
 def _names(pending) -> str:
     return str(sorted(f"{k}:v{r}" for k, r in pending)[:8])
+
+
+def _join(a: dict, b: dict) -> dict:
+    """Control-flow join: a register pending on either path, with the fewer loads
+    issued after it (the later possible landing)."""
+    out = dict(a)
+    for k, c in b.items():
+        out[k] = min(c, out[k]) if k in out else c
+    return out
 
 
 def check_kernel(name: str, lines) -> list:
@@ -150,18 +181,18 @@ def check_kernel(name: str, lines) -> list:
             return [f"{name}: '{t}': indirect control flow, not analysed"]
     blocks, succ = _blocks(ins)
     state_in = [None] * len(blocks)
-    state_in[0] = frozenset()
+    state_in[0] = {}
     work = [0]
     bad_all = []
     while work:
         i = work.pop()
-        pending = set(state_in[i])
+        pending = dict(state_in[i])
         bad = []
         b, e = blocks[i]
         for k in range(b, e + 1):
             pending = _step(ins[k][0], ins[k][1], pending, bad, name)
         for j in succ[i]:
-            new = frozenset(pending) | (state_in[j] or frozenset())
+            new = pending if state_in[j] is None else _join(state_in[j], pending)
             if state_in[j] is None or new != state_in[j]:
                 state_in[j] = new
                 work.append(j)
@@ -169,7 +200,7 @@ def check_kernel(name: str, lines) -> list:
     for i, (b, e) in enumerate(blocks):
         if state_in[i] is None:
             continue
-        pending = set(state_in[i])
+        pending = dict(state_in[i])
         for k in range(b, e + 1):
             pending = _step(ins[k][0], ins[k][1], pending, bad_all, name)
     return sorted(set(bad_all))
