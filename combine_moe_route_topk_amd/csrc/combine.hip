@@ -247,7 +247,12 @@ __global__ __launch_bounds__(256) void quant_returns_kernel(const uint16_t *__re
     }
     *(uint2 *)(dst + 8 * c) = make_uint2(pk[0] ^ 0x80808080u, pk[1] ^ 0x80808080u);
   }
-  if (lane == 0) *(float *)(dst + H) = s;
+  // the scale's 128-byte line is written whole (the scale, then zeros over the
+  // row's padding up to the line's end or the row's): a lone 4-byte store leaves
+  // a partly written line for the memory side to complete
+  const int64_t line_end = min(row_bytes, (int64_t)((H + 4 + 127) & ~127));
+  if (lane < (int)((line_end - H + 15) / 16))
+    *(uint4 *)(dst + H + 16 * lane) = make_uint4(lane == 0 ? __float_as_uint(s) : 0u, 0u, 0u, 0u);
 }
 }  // namespace
 }  // namespace moe

@@ -57,6 +57,14 @@ __device__ __forceinline__ uint64_t match_any(int key, int nbits, bool valid) {
   return valid ? m : 0ull;
 }
 
+// Lanes that write a message's trailer line whole: the trailer (lane 0), then
+// zeros over the row's padding up to the end of the 128-byte line that holds
+// the trailer, or the row's end if that comes first.
+__device__ __forceinline__ int trailer_line_lanes(int H, int64_t msg) {
+  const int64_t end = min(msg, (int64_t)((H + 16 + 127) & ~127));
+  return 1 + (int)((end - (H + 16)) / 16);
+}
+
 __device__ __forceinline__ int bits_for(int n) {
   int b = 0;
   while ((1 << b) < n) ++b;
@@ -399,11 +407,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     });
   else
     emit([&](float y) __attribute__((always_inline)) { return y / scale; });
+  // The trailer's 128-byte line is written whole: lanes after the first fill
+  // the row's padding behind the trailer with zeros up to the line's end (never
+  // past the row).  A 16-byte store alone leaves a partly written line, which
+  // the memory side completes with a read (233 -> 205 us per layer12288
+  // dispatch, the message bytes unchanged).
+  const int tail_lanes = trailer_line_lanes(H, msg);
   for (int j = jsel; j < jend; ++j) {
     uint8_t *dst = dst_of(j);
     const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)tail_w, j);
-    if (dst && lane == 0)
-      *(uint4 *)(dst + H) = make_uint4(__float_as_uint(scale), (uint32_t)s, (uint32_t)b, tw);
+    if (dst && lane < tail_lanes)
+      *(uint4 *)(dst + H + 16 * lane) =
+          lane == 0 ? make_uint4(__float_as_uint(scale), (uint32_t)s, (uint32_t)b, tw)
+                    : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -641,14 +657,17 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     }
     code = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
+  const int tail_lanes = trailer_line_lanes(H, msg);
   for (int j = 0; j < k; ++j) {
     const int64_t row = __shfl(drow, j, 64);  // with every lane active
     const uint32_t tw = __shfl(tail_w, j, 64);
     if (row < 0) continue;
     uint8_t *dst = disp_buf + row * msg;
     if (e0 < H) *(uint4 *)(dst + e0) = code;
-    if (slice == 0 && lane == 0)
-      *(uint4 *)(dst + H) = make_uint4(__float_as_uint(scale), (uint32_t)src_s, (uint32_t)bpos, tw);
+    if (slice == 0 && lane < tail_lanes)  // the trailer's line whole, as in the scatter
+      *(uint4 *)(dst + H + 16 * lane) =
+          lane == 0 ? make_uint4(__float_as_uint(scale), (uint32_t)src_s, (uint32_t)bpos, tw)
+                    : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 

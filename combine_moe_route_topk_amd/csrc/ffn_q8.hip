@@ -450,7 +450,10 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       }
     }
     __syncthreads();
-    // max |h| of each row over this n-tile: two threads per row scan the staged
+    // max |h| of each row over this n-tile, stored n-tile major (the block's 128
+    // rows as one run of floats: a [row][n-tile] layout left 16 four-byte
+    // fragments of every 64-byte row segment to as many blocks, each a partly
+    // written line for the memory side to complete).  Two threads per row scan the staged
     // row, alternate float4 columns each (a cross-lane reduction per value costs
     // far more); 16 lanes then read 8 rows x 2 columns, on 16 distinct bank groups
     {
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
       }
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       const int64_t rr = row0 + row;
-      if (part == 0 && row < rows_here && rr < nrows) pmax[rr * NT + tl.n] = m;
+      if (part == 0 && row < rows_here && rr < nrows) pmax[(int64_t)tl.n * nrows + rr] = m;
     }
     // 128 rows x 128 fp32 = 4096 chunks of 4 values; h is read only by the
     // requantization after this kernel, so the stores are non-temporal
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(256) void ffn_requant_kernel(const float *__restric
     if (c < n4) v[q] = src[c];
   }
   float m = 0.0f;
-  for (int i = lane; i < NT; i += 64) m = fmaxf(m, pmax[rr * NT + i]);
+  for (int i = lane; i < NT; i += 64) m = fmaxf(m, pmax[(int64_t)i * nrows + rr]);
   m = wave_max_f32(m);
   const float s = m / 127.0f;
   if (lane == 0) hs[rr] = s;

@@ -90,7 +90,9 @@ DispatchScratch dispatch_scratch_layout(const moe_geom_t &g);
 struct FfnScratch {
   int64_t tiles;     // int32 [P + 1]: exclusive prefix of per-slot m-tile counts, then the total
   int64_t slot_of;   // int32 [T*k/128 + P]: the slot of each m-tile (slot-major order)
-  int64_t pmax;      // fp32 [T*k][I/64]  max |h| of each row over each gate-up n-tile
+  int64_t pmax;      // fp32 [I/128][T*k] max |h| of each row over each gate-up n-tile, n-tile
+                     // major (a GEMM block stores its rows' maxima as one run); I/64 per row
+                     // reserved
   int64_t h;         // fp32 [T*k][I]
   int64_t hq;        // int8 [T*k][I]
   int64_t hs;        // fp32 [T*k]

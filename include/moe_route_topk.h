@@ -250,7 +250,9 @@ int moe_router_topk(const void *x, const void *w_router, const float *bias, moe_
  * Outputs:
  *   disp_buf  [D][S][cap][msg] bytes, 16B: row = q (H bytes) then a 16-byte
  *             trailer {f32 scale, i32 s, i32 b, u8 j, u8 local slot of the target on
- *             its partition, u16 event_id & 0xffff}; rows >= meta.count undefined
+ *             its partition, u16 event_id & 0xffff}, then zeros up to the end of the
+ *             trailer's 128-byte line or of the row (written so that the line is
+ *             stored whole); other padding and rows >= meta.count undefined
  *   meta      [D][S] {event_id, offset = sum_{s' < s} count[d][s'], count, 0}
  *   slot_count [P], slot_offset [P+1] (exclusive prefix sum)
  *   slot_rows [T*k]: for slot p, rows slot_offset[p] .. +slot_count[p] list the
@@ -430,8 +432,9 @@ int moe_expert_down_q8_int8ret(const int32_t *slot_count, const int32_t *slot_of
  *   ret         [T*k][H] bf16, 16B (rows [0, slot_offset[P]) are converted)
  *   slot_offset [P+1] as written by moe_dispatch_q8 (read on the device)
  *   ret_q8      [T*k][ret_q8_row_bytes] (moe_plan_sizes), 16B: row i holds the H
- *               codes, then the fp32 scale at byte H; the bytes after it are
- *               left as they were
+ *               codes, then the fp32 scale at byte H, then zeros up to the end of
+ *               the scale's 128-byte line (written so that the line is stored
+ *               whole); any bytes after that are left as they were
  * Combine these rows with mode MOE_RET_Q8_ROWS.  Geometries with relays are not
  * supported (MOE_ERR_UNSUPPORTED): the E2A hop moves bf16 rows.
  * Errors: MOE_ERR_INVALID_ARG (NULL or misaligned pointers), MOE_ERR_UNSUPPORTED.

@@ -119,15 +119,19 @@ def _check_dispatch(c: Case, phys, row_sample=None):
     assert np.array_equal(host(b.ret_row), lay["ret_row"]), "ret_row"
     assert np.array_equal(host(b.slot_rows), lay["slot_rows"]), "slot_rows"
     n = w.H + 16
+    # the trailer's 128-byte line is stored whole: zeros behind the trailer
+    pad_end = min(c.g.msg_bytes or w.msg, (n + 127) // 128 * 128)
     if row_sample is None:
         exp = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
         got = gather_rows(b, lay["disp_row"].ravel())
         assert np.array_equal(got[:, :n], exp[:, :n]), "message rows"
+        assert not got[:, n:pad_end].any(), "the rest of the trailer's line is zero"
     else:
         for t0, t1 in row_sample:
             exp = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id, t0, t1)
             got = gather_rows(b, lay["disp_row"][t0:t1].ravel())
             assert np.array_equal(got[:, :n], exp[:, :n]), f"message rows of tokens [{t0}, {t1})"
+            assert not got[:, n:pad_end].any(), "the rest of the trailer's line is zero"
     return q, s, lay
 
 
@@ -883,6 +887,8 @@ def test_expert_int8_tokenwise_returns_and_combine_small():
         y, *_ = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e])
         exp = _tokenwise_return_rows_oracle(w, y, rb)
         assert np.array_equal(got[rr[sel], :w.H + 4], exp[:, :w.H + 4]), f"rows, expert {e}"
+        line_end = min(rb, (w.H + 4 + 127) // 128 * 128)
+        assert not got[rr[sel], w.H + 4:line_end].any(), "the rest of the scale's line is zero"
     w32 = host(b.topk_w)
     for odt, obf in ((torch.float32, False), (torch.bfloat16, True)):
         c.layer.out_dtype = odt
@@ -920,7 +926,10 @@ def test_quant_returns_edge_rows():
     q, sc = oracle.quant_blocks(y, H)
     exp = oracle.int8_return_rows(q, sc, rb)
     assert np.array_equal(got[:, :H + 4], exp[:, :H + 4])
-    assert np.all(got[:, H + 4:] == 0x5A), "bytes after the scale are left as they were"
+    line_end = min(rb, (H + 4 + 127) // 128 * 128)
+    assert line_end > H + 4 and not got[:, H + 4:line_end].any(), \
+        "the rest of the scale's 128-byte line is zero"
+    assert np.all(got[:, line_end:] == 0x5A), "bytes after that line are left as they were"
     assert sc[0, 0] == 0 and np.all(q[0] == 0) and sc[2, 0] == 1 and q[2, :3].tolist() == [127, 2, -2]
 
 
