@@ -168,8 +168,56 @@ def time_pipeline(layer, x, lg, w, steps, warmup, n_micro=2):
     torch.cuda.empty_cache()
     return {"n_micro": n_micro, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(w.T / (ms * 1e-3), 1),
-            "note": "route + dispatch + experts + combine per microbatch on its own stream; "
-                    "the output equals the one-batch step's bit for bit"}
+            "note": "microbatches of T/2 tokens scheduled by MoeOverlap (route, dispatch and "
+                    "combine on one stream beside the other microbatch's experts on another); "
+                    "each microbatch's experts read every routed expert's weights; the output "
+                    "equals the one-batch step's bit for bit"}
+
+
+def time_batch_overlap(layer, x, lg, w, steps, warmup, n=2):
+    """A stream of whole batches of the workload (its tokens rolled by 0..n-1 rows,
+    in turn), each batch in one of n layers with their own static buffers: run one
+    after another on one stream, and submitted to MoeOverlap back to back (route,
+    dispatch and combine of one batch beside another's experts); mean time per
+    batch of each over `steps` batches."""
+    import torch
+    import combine_moe_route_topk_amd as moe
+    layers = [layer] + [moe.MoeLayer(layer.g, w.gating, layer.slot_partition,
+                                     layer.slot_logical, bias=layer.bias, weights=layer.weights,
+                                     I=w.I, out_dtype=torch.bfloat16) for _ in range(n - 1)]
+    inputs = [(x, lg)] + [(torch.roll(x, i, 0).contiguous(), torch.roll(lg, i, 0).contiguous())
+                          for i in range(1, n)]
+    ov = moe.MoeOverlap(layers)
+
+    def one_at_a_time(count):
+        for i in range(count):
+            layers[i % n].forward(*inputs[i % n])
+
+    def overlapped(count):
+        tickets = [ov.submit(*inputs[i % n]) for i in range(count)]
+        for t in tickets[-n:]:
+            t.wait()
+
+    def per_batch_us(fn):
+        fn(max(warmup, n))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(steps)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    seq_us = per_batch_us(one_at_a_time)
+    ovl_us = per_batch_us(overlapped)
+    del ov, layers[1:], inputs
+    torch.cuda.empty_cache()
+    return {"n_layers": n, "batches": steps, "ms_per_batch": round(ovl_us * 1e-3, 4),
+            "one_at_a_time_ms_per_batch": round(seq_us * 1e-3, 4),
+            "tokens_per_s": round(w.T / (ovl_us * 1e-6), 1),
+            "note": f"{steps} batches of {w.T} tokens submitted back to back to MoeOverlap over "
+                    f"{n} layers' buffers: each batch's route, dispatch and combine run beside "
+                    "another batch's experts; kernels that share the CUs slow each other"}
 
 
 def time_router(layer, x, w, steps, warmup):
@@ -225,6 +273,33 @@ def _median_us(fn, reps, warmup=3):
     return t[len(t) // 2]
 
 
+def _rate_us(fn, reps, warmup=3):
+    """Mean device time per call of fn() in microseconds over `reps` calls issued
+    back to back (one pair of events around all of them): the rate at which the
+    stream drains a steady stream of calls, host launch cost included."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def time_graph(layer, x, lg, mode, reps):
+    """Whole steps issued back to back, eagerly (one host call per kernel) and as
+    replays of the step captured once as a HIP graph (MoeLayer.capture)."""
+    eager_us = _rate_us(lambda: layer.forward(x, lg, combine=mode), reps)
+    graph = layer.capture(x, lg, combine=mode)
+    graph_us = _rate_us(graph.replay, reps)
+    del graph
+    return eager_us, graph_us
+
+
 def _bits(a, bf16=True):
     import numpy as np
     import torch
@@ -273,6 +348,7 @@ def time_decode96(reps):
     route_us = _median_us(lambda: layer.route(lg), reps)
     disp_us = _median_us(lambda: layer.dispatch(x), reps)
     comb_us = _median_us(lambda: layer.combine("q8"), reps)
+    step_us, graph_us = time_graph(layer, x, lg, "q8", reps)
     T, H, k = w.T, w.H, w.k
     db = T * H * 2 + T * k * 4 + T * k * (H + 16) + 3 * T * k * 4 + w.D * w.S * 16
     cb = T * k * (H + 4) + T * k * 8 + T * H * 4
@@ -281,6 +357,10 @@ def time_decode96(reps):
     return {"route_us": round(route_us, 2), "dispatch_us": round(disp_us, 2),
             "combine_us": round(comb_us, 2),
             "dispatch_plus_combine_us": round(disp_us + comb_us, 2),
+            "step_us": {"eager": round(step_us, 2), "graph": round(graph_us, 2),
+                        "note": "route + dispatch + combine issued back to back, mean per "
+                                "step: eager (one host call per kernel) and replayed as one "
+                                "HIP graph (MoeLayer.capture)"},
             "bytes": {"dispatch": db, "combine": cb},
             "frac_hbm_peak": round((db + cb) / ((disp_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "latency-bound (about 6.9 MB per call pair, cache-resident); median of "
@@ -568,7 +648,7 @@ def main():
                     help="time only the gate logits (moe_router_logits, moe_router_topk) on "
                          "the workload's hidden states: every gate launch then has that shape")
     ap.add_argument("--config-only", choices=("layer12288_uniform", "eplb4096", "decode96",
-                                              "twohop46080"),
+                                              "twohop46080", "batch_overlap"),
                     help="time only this workload's line of the configs (for profiling runs: "
                          "every launch then belongs to it); prints {workload, config}")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -595,6 +675,9 @@ def main():
             r = time_decode96(200)
         elif name == "twohop46080":
             r = time_twohop46080(max(5, args.steps // 5))
+        elif name == "batch_overlap":
+            layer, x, lg = build_layer(w)
+            r = time_batch_overlap(layer, x, lg, w, args.steps, args.warmup)
         else:
             # both take the headline layer's packed expert weights
             layer, x, lg = build_layer(w)
@@ -705,6 +788,18 @@ def main():
     # the microbatch pipeline: two halves of the sources on two streams
     result["microbatch_pipeline"] = time_pipeline(layer, x, lg, w, args.steps, args.warmup)
     log(f"[bench] 2-microbatch pipeline: {result['microbatch_pipeline']['ms_per_step']:.3f} ms/step")
+    result["batch_overlap"] = time_batch_overlap(layer, x, lg, w, args.steps, args.warmup)
+    log(f"[bench] whole batches in flight: {result['batch_overlap']['ms_per_batch']:.3f} ms/batch "
+        f"(one at a time {result['batch_overlap']['one_at_a_time_ms_per_batch']:.3f})")
+    # whole steps replayed as one captured HIP graph, beside the same steps issued eagerly
+    eg_us, gr_us = time_graph(layer, x, lg, "bf16", args.steps)
+    result["graph_replay"] = {
+        "ms_per_step": round(gr_us * 1e-3, 4), "tokens_per_s": round(w.T / (gr_us * 1e-6), 1),
+        "eager_ms_per_step": round(eg_us * 1e-3, 4),
+        "note": "MoeLayer.capture: the step captured once, replayed back to back; eager = the "
+                "same steps issued back to back without per-stage events"}
+    log(f"[bench] graph replay: {gr_us * 1e-3:.3f} ms/step (eager back to back "
+        f"{eg_us * 1e-3:.3f})")
     # the gate's logits from the hidden states (bf16 MFMA), timed alone:
     # the headline step starts from the logits, as the workload defines
     result["router"] = time_router(layer, x, w, args.steps, args.warmup)
@@ -723,7 +818,8 @@ def main():
         torch.cuda.empty_cache()
         cfg["decode96"] = time_decode96(200)
         log(f"[bench] decode96: dispatch {cfg['decode96']['dispatch_us']} us, "
-            f"combine {cfg['decode96']['combine_us']} us")
+            f"combine {cfg['decode96']['combine_us']} us, step {cfg['decode96']['step_us']['eager']} "
+            f"us eager / {cfg['decode96']['step_us']['graph']} us graph")
         cfg["twohop46080"] = time_twohop46080(max(5, args.steps // 5))
         log(f"[bench] twohop46080: A2E {cfg['twohop46080']['a2e_us']} us, "
             f"E2A {cfg['twohop46080']['e2a_us']} us")

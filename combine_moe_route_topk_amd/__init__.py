@@ -303,4 +303,5 @@ def moe_probe_mfma_i8(blocks: int, iters: int, out, stream=None):
     _check(lib().moe_probe_mfma_i8(blocks, iters, _ptr(out), _stream(stream)), "moe_probe_mfma_i8")
 
 
-from .layer import MoeBuffers, MoeLayer, MoePipeline, PackedExpertWeights  # noqa: E402,F401
+from .layer import (MoeBuffers, MoeGraph, MoeLayer, MoeOverlap, MoePipeline, MoeTicket,  # noqa: E402,F401,E501
+                    PackedExpertWeights)

@@ -303,28 +303,147 @@ class MoeLayer:
         token-wise before the combine."""
         self.route(logits)
         self.dispatch(x)
-        if self.weights is not None:
-            if combine == "q8blocks":
-                self.experts_gateup()
-                self.experts_down_int8ret()
-            else:
-                self.experts()
-                if combine == "q8rows":
-                    self.quant_returns()
+        self.expert_stage(combine)
         self.combine(combine)
         return self.buf.out
+
+    def expert_stage(self, combine: str = "bf16"):
+        """What forward runs between the dispatch and the combine: the experts (none
+        without weights), with INT8 block returns for 'q8blocks' and the token-wise
+        quantization of the returns for 'q8rows'."""
+        if self.weights is None:
+            return
+        if combine == "q8blocks":
+            self.experts_gateup()
+            self.experts_down_int8ret()
+        else:
+            self.experts()
+            if combine == "q8rows":
+                self.quant_returns()
+
+    def capture(self, x, logits, combine: str = "bf16") -> "MoeGraph":
+        """forward(x, logits, combine) captured once as a HIP graph.  The step runs
+        once eagerly first (kernel loading), then under capture on a side stream;
+        nothing in it allocates, synchronizes or sets memory from the host (every
+        clearing is a kernel).  Replays read x and logits where they are now: to run
+        other inputs, copy them into these tensors.  Not with debug_checks, whose
+        event check waits on the host."""
+        if self.debug_checks:
+            raise ValueError("capture: the debug event check waits on the host between kernels")
+        self.forward(x, logits, combine)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, logits, combine)
+        torch.cuda.synchronize()
+        return MoeGraph(graph, self.buf.out, self.event_id)
+
+
+class MoeGraph:
+    """One MoE step captured as a HIP graph (MoeLayer.capture): replay() reruns
+    route -> dispatch -> experts -> combine on the tensors the capture read and
+    the layer's static buffers, with no host work per kernel.  The dispatch
+    stamps the event id that was current at capture on every replay (event_id);
+    a caller that checks events captures one graph per id and alternates."""
+
+    def __init__(self, graph, out: torch.Tensor, event_id: int):
+        self.graph = graph
+        self.out = out
+        self.event_id = event_id
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.out
+
+
+class MoeTicket:
+    """One batch submitted to MoeOverlap: `out` is its output tensor (the layer's
+    buf.out), `done` the event recorded after its combine.  wait() makes the
+    current stream wait for it."""
+
+    def __init__(self, out: torch.Tensor, done):
+        self.out = out
+        self.done = done
+
+    def wait(self) -> torch.Tensor:
+        torch.cuda.current_stream().wait_event(self.done)
+        return self.out
+
+
+class MoeOverlap:
+    """Batches of one MoE layer in flight together [XDS, the overlap of
+    communication with computation across microbatches (P108-P111); CMI, the
+    microbatch section], on three default-priority streams: route and dispatch
+    on one, the experts on a second (the batches' expert stages one after
+    another), the combine on a third.  Each batch runs in one of the given
+    MoeLayers (its static buffers; the layers may share one
+    PackedExpertWeights), taken round robin, so one batch's route, dispatch
+    and combine run beside another batch's experts.
+
+    submit() orders a batch after the work already on the caller's stream (its
+    inputs) and after the previous batch that used the same layer; nothing
+    else waits, so successive submissions keep the expert stream busy.  A
+    batch's output stays valid until len(layers) more batches are submitted:
+    read it, on the caller's stream, before that.  Each output is its layer's
+    forward output bit for bit."""
+
+    def __init__(self, layers):
+        if not layers:
+            raise ValueError("MoeOverlap: at least one layer")
+        self.layers = list(layers)
+        dev = layers[0].slot_partition.device
+        self.comm = torch.cuda.Stream(device=dev)
+        self.compute = torch.cuda.Stream(device=dev)
+        self.ret = torch.cuda.Stream(device=dev)
+        self._next = 0
+        self._free = [None] * len(self.layers)
+
+    def submit(self, x, logits, combine: str = "bf16") -> MoeTicket:
+        j = self._next % len(self.layers)
+        self._next += 1
+        layer = self.layers[j]
+        ready = torch.cuda.Event()
+        ready.record(torch.cuda.current_stream())
+        self.comm.wait_event(ready)
+        if self._free[j] is not None:  # the layer's previous batch has been combined
+            self.comm.wait_event(self._free[j])
+        with torch.cuda.stream(self.comm):
+            layer.route(logits)
+            layer.dispatch(x)
+        routed = torch.cuda.Event()
+        routed.record(self.comm)
+        self.compute.wait_event(routed)
+        with torch.cuda.stream(self.compute):
+            layer.expert_stage(combine)
+        computed = torch.cuda.Event()
+        computed.record(self.compute)
+        self.ret.wait_event(computed)
+        with torch.cuda.stream(self.ret):
+            layer.combine(combine)
+        done = torch.cuda.Event()
+        done.record(self.ret)
+        self._free[j] = done
+        return MoeTicket(layer.buf.out, done)
+
+    def forward(self, inputs, combine: str = "bf16"):
+        """inputs: one (x, logits) per batch, at most one per layer.  Submits them
+        all, then the caller's stream waits for every one.  Returns the outputs."""
+        if len(inputs) > len(self.layers):
+            raise ValueError(f"{len(inputs)} batches for {len(self.layers)} layers")
+        tickets = [self.submit(x, logits, combine) for x, logits in inputs]
+        return [t.wait() for t in tickets]
 
 
 class MoePipeline:
     """A microbatch pipeline of one MoE layer on one GPU [XDS, the microbatch
     overlap of communication with computation (P108-P111); CMI, the microbatch
     section].  The batch is split by source partitions into n microbatches,
-    each with its own static buffers and its own (default-priority) stream, so
-    one microbatch's route and dispatch can run while another is in its
-    experts.  Every token's result is independent of the split (routes,
-    replica rotation by batch position, quantization, expert rows and the
-    combine are per token), so the output equals MoeLayer.forward's bit for
-    bit.  Orchestration only: every step runs in the library's kernels."""
+    each with its own static buffers, run as MoeOverlap schedules them: one
+    microbatch's route and dispatch, and another's combine, beside a third's
+    experts.  Every token's result is independent of the split (routes, replica
+    rotation by batch position, quantization, expert rows and the combine are
+    per token), so the output equals MoeLayer.forward's bit for bit.
+    Orchestration only: every step runs in the library's kernels."""
 
     def __init__(self, g: Geom, n_micro: int, gating: str, slot_partition: torch.Tensor,
                  slot_logical: torch.Tensor, replica_offsets: Optional[torch.Tensor] = None,
@@ -339,29 +458,19 @@ class MoePipeline:
         sub = Geom(g.T // n_micro, g.H, g.E, g.P, g.k, g.D, g.Epp, g.S // n_micro, g.LB,
                    g.msg_bytes, 0, 0)
         self.tm = sub.T
-        self.layers = [MoeLayer(sub, gating, slot_partition, slot_logical, replica_offsets,
-                                replica_slots, bias, weights, I, out_dtype)
-                       for _ in range(n_micro)]
-        self.streams = [torch.cuda.Stream() for _ in range(n_micro)]
+        layers = [MoeLayer(sub, gating, slot_partition, slot_logical, replica_offsets,
+                           replica_slots, bias, weights, I, out_dtype)
+                  for _ in range(n_micro)]
         self.out = torch.empty((g.T, g.H), dtype=out_dtype, device=slot_partition.device)
-        for i, layer in enumerate(self.layers):
+        for i, layer in enumerate(layers):
             layer.buf.out = self.out[i * sub.T:(i + 1) * sub.T]
+        self.overlap = MoeOverlap(layers)
+        self.layers = self.overlap.layers
 
     def forward(self, x, logits, combine: str = "bf16"):
-        """route -> dispatch -> experts -> combine of each microbatch on its stream;
-        the caller's stream waits for all of them."""
-        cur = torch.cuda.current_stream()
-        start = torch.cuda.Event()
-        start.record(cur)
-        done = []
-        for i, (layer, s) in enumerate(zip(self.layers, self.streams)):
-            s.wait_event(start)
-            with torch.cuda.stream(s):
-                layer.forward(x[i * self.tm:(i + 1) * self.tm], logits[i * self.tm:(i + 1) * self.tm],
-                              combine)
-            ev = torch.cuda.Event()
-            ev.record(s)
-            done.append(ev)
-        for ev in done:
-            cur.wait_event(ev)
+        """The microbatches through MoeOverlap; the caller's stream waits for all of
+        them.  Returns the [T][H] output."""
+        tm = self.tm
+        self.overlap.forward([(x[i * tm:(i + 1) * tm], logits[i * tm:(i + 1) * tm])
+                              for i in range(self.n)], combine)
         return self.out

@@ -950,8 +950,8 @@ def test_layer_int8_tokenwise_returns_small_end_to_end():
 
 @pytest.mark.parametrize("name,n_micro", [("ffn_small", 2), ("ragged", 3)])
 def test_microbatch_pipeline_equals_one_batch(name, n_micro):
-    """The microbatch pipeline (one microbatch per source partition group, each
-    on its own stream) gives the single-batch layer's output bit for bit, twice
+    """The microbatch pipeline (one microbatch per source partition group,
+    scheduled by MoeOverlap on a communication and a compute stream) gives the single-batch layer's output bit for bit, twice
     in a row, and matches the oracle's whole layer within the output tolerance;
     ffn_small runs the INT8 SwiGLU experts, ragged identity experts with the
     INT8 combine."""
@@ -979,6 +979,86 @@ def test_microbatch_pipeline_equals_one_batch(name, n_micro):
             assert_close(got, bf16_to_f32(r["out"]), BF16_RTOL, BF16_ATOL, "pipeline vs oracle")
         else:
             assert_close(host(out), r["out"], FP32_RTOL, FP32_ATOL, "pipeline vs oracle")
+
+
+@pytest.mark.parametrize("name,mode,n", [("ffn_small", "bf16", 2), ("ffn_small", "q8blocks", 3),
+                                         ("ffn_small", "q8rows", 2), ("ragged", "q8", 3)])
+def test_overlap_of_whole_batches_equals_one_at_a_time(name, mode, n):
+    """MoeOverlap: n batches in flight on a communication and a compute stream
+    (each batch's route, dispatch and combine beside another batch's experts)
+    give every batch the output of its own step run alone, bit for bit, on two
+    calls in a row; the batches are the workload's tokens rolled by 0, 1, 2 rows."""
+    w = FFN_SMALL if name == "ffn_small" else RAGGED
+    if w.experts == "swiglu":
+        c, _, _, _ = _ffn_case(w)
+    else:
+        c = Case(w)
+    inputs = [(torch.roll(c.x_d, i, 0).contiguous(), torch.roll(c.lg_d, i, 0).contiguous())
+              for i in range(n)]
+
+    def bits(t):
+        return t.view(torch.int16).clone() if t.dtype == torch.bfloat16 else t.clone()
+
+    refs = [bits(c.layer.forward(x, lg, combine=mode)) for x, lg in inputs]
+    torch.cuda.synchronize()
+    layers = [moe.MoeLayer(c.g, w.gating, c.layer.slot_partition, c.layer.slot_logical,
+                           c.layer.replica_offsets, c.layer.replica_slots, c.layer.bias,
+                           c.layer.weights, w.I, c.layer.out_dtype) for _ in range(n)]
+    ov = moe.MoeOverlap(layers)
+    for call in range(2):
+        _log(f"[overlap] {name} {mode} n={n} call {call}")
+        outs = ov.forward(inputs, combine=mode)
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(bits(o), r), f"batch {i}, call {call}"
+
+
+@pytest.mark.parametrize("name,mode", [("ffn_small", "bf16"), ("ffn_small", "q8rows"),
+                                       ("ffn_small", "q8blocks"), ("ragged", "q8"),
+                                       ("twohop_small", "bf16")])
+def test_layer_graph_replay_equals_eager(name, mode):
+    """MoeLayer.capture: the whole step captured once as a HIP graph gives the
+    eager step's output bit for bit on every replay, with eager steps of another
+    input and host synchronizations between the replays, and follows new inputs
+    copied into the captured tensors (rows and logits rolled by one token)."""
+    w = {"ffn_small": FFN_SMALL, "ragged": RAGGED, "twohop_small": TWOHOP_SMALL}[name]
+    if w.experts == "swiglu":
+        c, _, _, _ = _ffn_case(w)
+    else:
+        c = Case(w)
+        if w.experts == "synthetic":  # no experts: the combine reads fixed return rows
+            gen = torch.Generator(device="cuda").manual_seed(7)
+            ret = c.layer.buf.ret
+            ret.copy_(torch.randn(ret.shape, generator=gen, device="cuda",
+                                  dtype=torch.bfloat16).view(torch.int16))
+
+    def bits(t):
+        return t.view(torch.int16).clone() if t.dtype == torch.bfloat16 else t.clone()
+
+    xin, lin = c.x_d.clone(), c.lg_d.clone()
+    x2, l2 = torch.roll(xin, 1, 0).contiguous(), torch.roll(lin, 1, 0).contiguous()
+    ref1 = bits(c.layer.forward(xin, lin, combine=mode))
+    ref2 = bits(c.layer.forward(x2, l2, combine=mode))
+    torch.cuda.synchronize()
+    assert not torch.equal(ref1, ref2)
+    graph = c.layer.capture(xin, lin, combine=mode)
+    with pytest.raises(ValueError):
+        moe.MoeLayer(c.g, w.gating, c.layer.slot_partition, c.layer.slot_logical,
+                     debug_checks=True).capture(xin, lin, combine=mode)
+    x1, l1 = xin.clone(), lin.clone()
+    for i in range(3):
+        _log(f"[graph] {name} {mode} replay {i}")
+        out = graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), ref1), f"replay {i}"
+        assert torch.equal(bits(c.layer.forward(x2, l2, combine=mode)), ref2), f"eager {i}"
+        torch.cuda.synchronize()
+        xin.copy_(x2)
+        lin.copy_(l2)
+        assert torch.equal(bits(graph.replay()), ref2), f"replay {i} of the rolled input"
+        xin.copy_(x1)
+        lin.copy_(l1)
+        torch.cuda.synchronize()
 
 
 def test_expert_ffn_layer12288_sampled_rows():
