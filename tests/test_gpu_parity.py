@@ -1013,6 +1013,34 @@ def test_overlap_of_whole_batches_equals_one_at_a_time(name, mode, n):
             assert torch.equal(bits(o), r), f"batch {i}, call {call}"
 
 
+def test_overlap_streaming_submissions_reuse_layers_in_turn():
+    """MoeOverlap.submit: seven batches over two layers' buffers, each output copied
+    on the caller's stream right after its ticket (before the layer is reused two
+    submissions later), equal the steps run alone bit for bit; more batches than
+    layers in one forward() are refused."""
+    w = FFN_SMALL
+    c, _, _, _ = _ffn_case(w)
+    inputs = [(torch.roll(c.x_d, 3 * i, 0).contiguous(), torch.roll(c.lg_d, 5 * i, 0).contiguous())
+              for i in range(7)]
+    refs = [c.layer.forward(x, lg).view(torch.int16).clone() for x, lg in inputs]
+    torch.cuda.synchronize()
+    layers = [moe.MoeLayer(c.g, w.gating, c.layer.slot_partition, c.layer.slot_logical,
+                           bias=c.layer.bias, weights=c.layer.weights, I=w.I) for _ in range(2)]
+    ov = moe.MoeOverlap(layers)
+    got = []
+    pending = []
+    for x, lg in inputs:
+        pending.append(ov.submit(x, lg))
+        if len(pending) == 2:  # the oldest batch's layer is taken by the next submission
+            got.append(pending.pop(0).wait().view(torch.int16).clone())
+    got += [t.wait().view(torch.int16).clone() for t in pending]
+    torch.cuda.synchronize()
+    for i, (g_, r) in enumerate(zip(got, refs)):
+        assert torch.equal(g_, r), f"batch {i}"
+    with pytest.raises(ValueError):
+        ov.forward(inputs[:3])
+
+
 @pytest.mark.parametrize("name,mode", [("ffn_small", "bf16"), ("ffn_small", "q8rows"),
                                        ("ffn_small", "q8blocks"), ("ragged", "q8"),
                                        ("twohop_small", "bf16")])
