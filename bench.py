@@ -102,12 +102,18 @@ def build_layer(w, log_every=64):
 
 
 def time_gpu(layer, x, lg, steps, warmup, returns="bf16", flush=None):
-    """Per-stage and per-step times of `steps` whole steps.  returns: 'bf16' (the
+    """Per-step and per-stage times of `steps` whole steps.  returns: 'bf16' (the
     workload's expert returns), 'q8blocks' (INT8 returns, one scale per 256
     columns, quantized in the down projection's epilogue) or 'q8rows' (token-wise
     INT8 returns: one scale per row, quantized by moe_quant_returns_q8).  With
     `flush` (a device buffer), the buffer is overwritten before every step, outside
-    the timed stages, so that each step starts with cold caches."""
+    the timed steps, so that each step starts with cold caches.
+
+    The steps are timed twice.  First with one event at each step boundary (a pair
+    around each step with `flush`), which gives the step time and its spread; then
+    again with a pair of events around every stage, which gives the stage times.
+    Events between the stages add time of their own, so the step time comes from
+    the first pass."""
     import torch
     down = {"bf16": layer.experts_down, "q8rows": layer.experts_down,
             "q8blocks": layer.experts_down_int8ret}[returns]
@@ -118,32 +124,51 @@ def time_gpu(layer, x, lg, steps, warmup, returns="bf16", flush=None):
     if returns == "q8rows":
         stages.append(("quant_returns", layer.quant_returns))
     stages.append(("combine", lambda: layer.combine(returns)))
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     for _ in range(warmup):
         for _, f in stages:
             f()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in stages] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # pass 1: whole steps
+    marks = [(ev(), ev()) if flush is not None else (ev(), None) for _ in range(steps)]
+    last = ev()
     torch.cuda.synchronize()
-    start.record()
+    for s, (a, b) in enumerate(marks):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        a.record()
+        for _, f in stages:
+            f()
+        if b is not None:
+            b.record()
+    last.record()
+    torch.cuda.synchronize()
+    if flush is None:
+        ends = [m[0] for m in marks[1:]] + [last]
+        step_ms = [a.elapsed_time(e) for (a, _), e in zip(marks, ends)]
+        ms = marks[0][0].elapsed_time(last) / steps
+    else:
+        step_ms = [a.elapsed_time(b) for a, b in marks]
+        ms = sum(step_ms) / steps
+    step_ms.sort()
+    q = lambda f: step_ms[min(len(step_ms) - 1, int(f * len(step_ms)))]
+    dist = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+    # pass 2: every stage between its own pair of events
+    evs = [[(ev(), ev()) for _ in stages] for _ in range(steps)]
+    torch.cuda.synchronize()
     for s in range(steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
-        for (name, f), (a, b) in zip(stages, ev[s]):
+        for (name, f), (a, b) in zip(stages, evs[s]):
             a.record()
             f()
             b.record()
-    end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    per = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
+    per = {name: sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
            for i, (name, _) in enumerate(stages)}
-    # per-step wall time on the stream: first stage start -> last stage end
-    step_ms = sorted(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(steps))
-    q = lambda f: step_ms[min(len(step_ms) - 1, int(f * len(step_ms)))]
-    dist = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
-    ms = total_ms / steps if flush is None else sum(step_ms) / steps
     return ms, per, dist
 
 
