@@ -588,6 +588,50 @@ def test_combine_q8_identity_experts(name):
     assert np.all(np.abs(host(out2) - xf) <= s[:, None] * 0.5 + 1e-5 * np.abs(xf) + 1e-6)
 
 
+def _random_geometries(n=24, seed=20261202):
+    """Seeded small geometries across the ABI's ranges: E from 1 to 512 (whole and
+    partial 64-lane runs of the top-k), k from 1 to min(16, E), 1-4 slots per
+    partition, H any multiple of 16 up to 1520, 1-5 sources of 1-49 tokens, both
+    gatings and both input types, with and without the Zipf bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 5, 8, 13, 31, 64, 100, 257, 512]))
+        k = int(rng.integers(1, min(16, E) + 1))
+        Epp = int(rng.integers(1, 5))
+        S, LB = int(rng.integers(1, 6)), int(rng.integers(1, 50))
+        out.append(mw.Workload(
+            f"rand{i}", T=S * LB, H=16 * int(rng.integers(1, 96)), E=E, P=E, k=k,
+            D=(E + Epp - 1) // Epp, Epp=Epp, S=S, LB=LB,
+            gating=str(rng.choice(["softmax", "sigmoid"])),
+            logits_dtype=str(rng.choice(["f32", "bf16"])), x_dtype=str(rng.choice(["f32", "bf16"])),
+            zipf=bool(rng.integers(0, 2)), experts="identity", combine="q8", out_dtype="f32",
+            seed=int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_geometries(), ids=lambda w: w.name)
+def test_random_geometries_route_dispatch_combine(w):
+    """Twenty-four seeded geometries: routing, the dispatch layout and message rows
+    bit-exact against the oracle, and the INT8 combine of the dispatched rows
+    bit-exact in fp32 and bf16 given the oracle's weights."""
+    _log(f"[random] {w}")
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    q, s, lay = _check_dispatch(c, phys)
+    b = c.layer.buf
+    rows = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    w32 = tw.astype(np.float32)
+    for bf, dt in ((False, moe.DTYPE_F32), (True, moe.DTYPE_BF16)):
+        ref = oracle.combine(rows, ident, w32, w.k, w.H, "q8", bf, scale_offset=w.H)
+        out = torch.empty((w.T, w.H), dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+        moe.moe_combine(moe.RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, to_dev(w32), c.g, dt, out)
+        torch.cuda.synchronize()
+        got = host(out.view(torch.int16)).view(np.uint16) if bf else host(out)
+        assert np.array_equal(got, ref), f"combine ({'bf16' if bf else 'fp32'} output)"
+
+
 # the ABI's limits: H = MOE_MAX_H (the scatter's sixteen 1024-element slices per
 # row), k = MOE_MAX_K, E = P = D = 1024 (the top-k's sixteen experts per lane);
 # 3072 routes take the count / scan / scatter path, 1024 the one-launch path
