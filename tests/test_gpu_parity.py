@@ -764,14 +764,11 @@ def _ffn_case(w):
     return c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd)
 
 
-def test_expert_ffn_parity_small():
-    """Grouped INT8 SwiGLU: int32 accumulators of both GEMMs bit-exact, and the
-    bf16 return rows bit-exact (the same fp32 epilogue on both sides)."""
-    w = FFN_SMALL
-    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
-    sc = lay["slot_count"]
-    assert sc.max() > 256, "want a slot spanning three 128-row m-tiles"
-    assert 0 < sc[sc > 0].min() < 32, "want a slot smaller than one 32-row MFMA block"
+def _check_expert_ffn(c, phys, q, s, lay, weights):
+    """Both GEMMs' int32 accumulators and the bf16 return rows of every routed
+    row bit-exact against the oracle's expert FFN of the same rows."""
+    w = c.w
+    wgu, sgu, wd, sd = weights
     n = w.T * w.k
     acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
     acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
@@ -790,6 +787,17 @@ def test_expert_ffn_parity_small():
         assert np.array_equal(agu[rr[sel]], o_gu), f"gate/up accumulators, expert {e}"
         assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
         assert np.array_equal(ret[rr[sel]], y), f"return rows, expert {e}"
+
+
+def test_expert_ffn_parity_small():
+    """Grouped INT8 SwiGLU: int32 accumulators of both GEMMs bit-exact, and the
+    bf16 return rows bit-exact (the same fp32 epilogue on both sides)."""
+    w = FFN_SMALL
+    c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
+    sc = lay["slot_count"]
+    assert sc.max() > 256, "want a slot spanning three 128-row m-tiles"
+    assert 0 < sc[sc > 0].min() < 32, "want a slot smaller than one 32-row MFMA block"
+    _check_expert_ffn(c, phys, q, s, lay, (wgu, sgu, wd, sd))
 
 
 # expert GEMMs at the ABI's widths: I = 4096 and I = 16384 (the requantization
@@ -813,24 +821,35 @@ def test_expert_ffn_parity_at_the_abi_widths(w):
     """Both GEMMs' int32 accumulators and the bf16 return rows bit-exact at the
     widest H and I the ABI takes."""
     c, (ids, tw, phys), (q, s, lay), (wgu, sgu, wd, sd) = _ffn_case(w)
-    n = w.T * w.k
-    acc_gu = torch.empty((n, 2 * w.I), dtype=torch.int32, device="cuda")
-    acc_d = torch.empty((n, w.H), dtype=torch.int32, device="cuda")
-    c.layer.experts(acc_gu, acc_d)
-    torch.cuda.synchronize()
-    b = c.layer.buf
-    logical = c.sl[phys.ravel()]
-    ret = host(b.ret.view(torch.int16)).view(np.uint16)
-    agu, ad = host(acc_gu), host(acc_d)
-    rr = lay["ret_row"].ravel()
-    for e in np.unique(logical):
-        sel = np.nonzero(logical == e)[0]
-        toks = sel // w.k
-        y, hq, hs, o_gu, o_d = oracle.expert_ffn(q[toks], s[toks], wgu[e], sgu[e], wd[e], sd[e],
-                                                 want_acc=True)
-        assert np.array_equal(agu[rr[sel]], o_gu), f"gate/up accumulators, expert {e}"
-        assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
-        assert np.array_equal(ret[rr[sel]], y), f"return rows, expert {e}"
+    _check_expert_ffn(c, phys, q, s, lay, (wgu, sgu, wd, sd))
+
+
+def _random_ffn_geometries(n=10, seed=7051):
+    """Seeded small expert-FFN geometries: H any multiple of 128 up to 1024, I any
+    multiple of 64 up to 1024, 2-24 experts, k up to min(6, E), 1-4 slots per
+    partition, 1-3 sources of 10-80 tokens, with and without the Zipf bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(2, 25))
+        Epp = int(rng.integers(1, 5))
+        S, LB = int(rng.integers(1, 4)), int(rng.integers(10, 81))
+        out.append(mw.Workload(
+            f"ffnrand{i}", T=S * LB, H=128 * int(rng.integers(1, 9)), E=E, P=E,
+            k=int(rng.integers(1, min(6, E) + 1)), D=(E + Epp - 1) // Epp, Epp=Epp, S=S, LB=LB,
+            gating="sigmoid", logits_dtype="bf16", x_dtype=str(rng.choice(["f32", "bf16"])),
+            zipf=bool(rng.integers(0, 2)), experts="swiglu", combine="bf16", out_dtype="bf16",
+            I=64 * int(rng.integers(1, 17)), seed=int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_ffn_geometries(), ids=lambda w: w.name)
+def test_random_geometries_expert_ffn(w):
+    """Ten seeded expert-FFN geometries: int32 accumulators and bf16 return rows
+    bit-exact against the oracle."""
+    _log(f"[random ffn] {w}")
+    c, (ids, tw, phys), (q, s, lay), weights = _ffn_case(w)
+    _check_expert_ffn(c, phys, q, s, lay, weights)
 
 
 def test_layer_ffn_small_end_to_end():
