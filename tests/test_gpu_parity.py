@@ -632,6 +632,47 @@ def test_random_geometries_route_dispatch_combine(w):
         assert np.array_equal(got, ref), f"combine ({'bf16' if bf else 'fp32'} output)"
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_replica_maps_route_dispatch_combine(i):
+    """EPLB gather with seeded random replica maps: every expert keeps one slot and
+    1..E extra slots go to random experts, the physical slot ids are shuffled, and
+    the slots are dealt to partitions at random (at most Epp each).  Physical ids
+    (R_e[b mod |R_e|]), the dispatch layout and rows, and the INT8 combine are
+    bit-exact against the oracle on the same maps."""
+    rng = np.random.default_rng(9000 + i)
+    E = int(rng.choice([4, 9, 16, 33, 64]))
+    extra = int(rng.integers(1, E + 1))
+    P, Epp = E + extra, int(rng.integers(1, 4))
+    S, LB = int(rng.integers(1, 4)), int(rng.integers(5, 60))
+    w = mw.Workload(f"rmap{i}", T=S * LB, H=16 * int(rng.integers(1, 40)), E=E, P=P,
+                    k=int(rng.integers(1, min(8, E) + 1)), D=(P + Epp - 1) // Epp, Epp=Epp, S=S,
+                    LB=LB, gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=True,
+                    experts="identity", combine="q8", out_dtype="f32", seed=int(rng.integers(1 << 30)))
+    sl = np.r_[np.arange(E), rng.integers(0, E, extra)].astype(np.int32)[rng.permutation(P)]
+    sp = rng.permutation(np.arange(P) // Epp).astype(np.int32)
+    ro = np.zeros(E + 1, np.int32)
+    ro[1:] = np.cumsum(np.bincount(sl, minlength=E))
+    rs = np.argsort(sl, kind="stable").astype(np.int32)  # each expert's slots, ascending
+    _log(f"[replica map] {w} copies {np.bincount(sl, minlength=E).tolist()}")
+    c = Case(w)
+    c.ro, c.rs, c.sp, c.sl, c.use_map = ro, rs, sp, sl, True
+    c.layer = moe.MoeLayer(c.g, w.gating, to_dev(sp), to_dev(sl), to_dev(ro), to_dev(rs),
+                           to_dev(c.bias), None, 0, torch.float32)
+    ids, tw, phys = _check_route(c)
+    assert np.array_equal(sl[phys], ids), "every route lands on a replica of its expert"
+    q, s, lay = _check_dispatch(c, phys)
+    rows = oracle.dispatch_rows(w, q, s, phys, lay["slot_local"], c.event_id)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    w32 = tw.astype(np.float32)
+    ref = oracle.combine(rows, ident, w32, w.k, w.H, "q8", False, scale_offset=w.H)
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    b = c.layer.buf
+    moe.moe_combine(moe.RET_Q8_FROM_DISPATCH, b.disp_buf, b.disp_row, to_dev(w32), c.g,
+                    moe.DTYPE_F32, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), ref), "combine"
+
+
 # the ABI's limits: H = MOE_MAX_H (the scatter's sixteen 1024-element slices per
 # row), k = MOE_MAX_K, E = P = D = 1024 (the top-k's sixteen experts per lane);
 # 3072 routes take the count / scan / scatter path, 1024 the one-launch path
