@@ -452,6 +452,38 @@ def test_dispatch_twohop_small_equals_direct():
                           gather_rows(direct.layer.buf, rows)[:, :n])
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_random_twohop_geometries(i):
+    """Seeded two-hop geometries (one slot per partition, 1..E redundant slots, 1..D-1
+    relay partitions): the layout and rows after the second hop bit-exact against
+    the oracle's one-hop layout, and the E2A relay plus combine of synthetic bf16
+    returns bit-exact against the oracle's combine of the same rows."""
+    rng = np.random.default_rng(4242 + i)
+    E = int(rng.choice([6, 10, 17, 30]))
+    budget = int(rng.integers(1, E + 1))
+    P = E + budget
+    S, LB = int(rng.integers(1, 6)), int(rng.integers(5, 51))
+    w = mw.Workload(f"twohop_rand{i}", T=S * LB, H=16 * int(rng.integers(1, 33)), E=E, P=P,
+                    k=int(rng.integers(1, min(8, E) + 1)), D=P, Epp=1, S=S, LB=LB,
+                    gating="sigmoid", logits_dtype="bf16", x_dtype="bf16", zipf=bool(i % 2),
+                    experts="synthetic", combine="bf16", out_dtype="bf16", eplb="first32",
+                    budget=budget, relays=int(rng.integers(1, P)), seed=int(rng.integers(1 << 30)))
+    _log(f"[twohop random] {w}")
+    c = Case(w)
+    ids, tw, phys = _check_route(c)
+    _check_dispatch(c, phys)
+    b = c.layer.buf
+    rets = mw.route_returns(w)
+    rr = torch.from_numpy(host(b.ret_row).ravel().astype(np.int64)).cuda()
+    b.ret[: w.T * w.k].index_copy_(0, rr, torch.from_numpy(rets.view(np.int16)).cuda())
+    c.layer.combine("bf16")
+    torch.cuda.synchronize()
+    out = host(b.out.view(torch.int16)).view(np.uint16)
+    ident = np.arange(w.T * w.k, dtype=np.int32).reshape(w.T, w.k)
+    ref = oracle.combine(rets, ident, host(b.topk_w), w.k, w.H, "bf16", True)
+    assert np.array_equal(out, ref), "E2A relay + combine"
+
+
 def test_dispatch_twohop46080_full_layout_all_rows():
     """46080 tokens from 160 sources to 288 partitions through 160 relays: full
     layout, and every one of the 368,640 message rows (checked in token chunks)."""
