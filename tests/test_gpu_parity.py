@@ -852,6 +852,7 @@ def _check_expert_ffn(c, phys, q, s, lay, weights):
     ret = host(b.ret.view(torch.int16)).view(np.uint16)
     agu, ad = host(acc_gu), host(acc_d)
     rr = lay["ret_row"].ravel()
+    ys = {}  # expert -> (its return rows, the oracle's bf16 rows)
     for e in np.unique(logical):
         sel = np.nonzero(logical == e)[0]
         toks = sel // w.k
@@ -860,6 +861,8 @@ def _check_expert_ffn(c, phys, q, s, lay, weights):
         assert np.array_equal(agu[rr[sel]], o_gu), f"gate/up accumulators, expert {e}"
         assert np.array_equal(ad[rr[sel]], o_d), f"down accumulators, expert {e}"
         assert np.array_equal(ret[rr[sel]], y), f"return rows, expert {e}"
+        ys[e] = (rr[sel], y)
+    return ys
 
 
 def test_expert_ffn_parity_small():
@@ -919,10 +922,29 @@ def _random_ffn_geometries(n=10, seed=7051):
 @pytest.mark.parametrize("w", _random_ffn_geometries(), ids=lambda w: w.name)
 def test_random_geometries_expert_ffn(w):
     """Ten seeded expert-FFN geometries: int32 accumulators and bf16 return rows
-    bit-exact against the oracle."""
+    bit-exact against the oracle, and both INT8 return encodings of those rows
+    (one scale per 256 columns from the down epilogue, one per row from the
+    quantize pass; an odd multiple of 128 for H leaves the last block half full)
+    bit-exact."""
     _log(f"[random ffn] {w}")
     c, (ids, tw, phys), (q, s, lay), weights = _ffn_case(w)
-    _check_expert_ffn(c, phys, q, s, lay, weights)
+    ys = _check_expert_ffn(c, phys, q, s, lay, weights)
+    b = c.layer.buf
+    rb = b.sizes.ret_q8_row_bytes
+    c.layer.quant_returns()
+    torch.cuda.synchronize()
+    tokenwise = host(b.ret_q8_rows()).copy()
+    c.layer.experts_gateup()
+    c.layer.experts_down_int8ret()
+    torch.cuda.synchronize()
+    blocks = host(b.ret_q8_rows())
+    nb = w.H + 4 * ((w.H + moe.RET_Q8_BLOCK - 1) // moe.RET_Q8_BLOCK)
+    for e, (rows, y) in ys.items():
+        exp = _int8_return_rows_oracle(w, y, rb)
+        assert np.array_equal(blocks[rows, :nb], exp[:, :nb]), f"block-scaled INT8 rows, expert {e}"
+        expr = _tokenwise_return_rows_oracle(w, y, rb)
+        assert np.array_equal(tokenwise[rows, :w.H + 4], expr[:, :w.H + 4]), \
+            f"token-wise INT8 rows, expert {e}"
 
 
 def test_layer_ffn_small_end_to_end():
