@@ -336,7 +336,7 @@ class MoeLayer:
         with torch.cuda.graph(graph):
             self.forward(x, logits, combine)
         torch.cuda.synchronize()
-        return MoeGraph(graph, self.buf.out, self.event_id)
+        return MoeGraph(graph, self.buf.out, self.event_id, (x, logits))
 
 
 class MoeGraph:
@@ -344,12 +344,14 @@ class MoeGraph:
     route -> dispatch -> experts -> combine on the tensors the capture read and
     the layer's static buffers, with no host work per kernel.  The dispatch
     stamps the event id that was current at capture on every replay (event_id);
-    a caller that checks events captures one graph per id and alternates."""
+    a caller that checks events captures one graph per id and alternates.  The
+    graph holds the captured inputs, whose memory every replay reads."""
 
-    def __init__(self, graph, out: torch.Tensor, event_id: int):
+    def __init__(self, graph, out: torch.Tensor, event_id: int, inputs):
         self.graph = graph
         self.out = out
         self.event_id = event_id
+        self.inputs = inputs
 
     def replay(self) -> torch.Tensor:
         self.graph.replay()
@@ -400,11 +402,20 @@ class MoeOverlap:
 
     def submit(self, x, logits, combine: str = "bf16") -> MoeTicket:
         j = self._next % len(self.layers)
-        self._next += 1
         layer = self.layers[j]
+        g = layer.g
+        _require("x", x, (g.T, g.H), _BF16_BITS + (torch.float32,))  # before any work is queued
+        _require("logits", logits, (g.T, g.E), _BF16_BITS + (torch.float32,))
+        if combine not in ("q8", "bf16", "q8blocks", "q8rows"):
+            raise ValueError(f"combine {combine!r}")
+        self._next += 1
         ready = torch.cuda.Event()
         ready.record(torch.cuda.current_stream())
         self.comm.wait_event(ready)
+        # the inputs are read on the communication stream: their memory must not
+        # go back to the caller's stream before that read is done
+        x.record_stream(self.comm)
+        logits.record_stream(self.comm)
         if self._free[j] is not None:  # the layer's previous batch has been combined
             self.comm.wait_event(self._free[j])
         with torch.cuda.stream(self.comm):

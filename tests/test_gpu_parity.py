@@ -1197,6 +1197,9 @@ def test_overlap_streaming_submissions_reuse_layers_in_turn():
         assert torch.equal(g_, r), f"batch {i}"
     with pytest.raises(ValueError):
         ov.forward(inputs[:3])
+    with pytest.raises(ValueError):  # refused before anything is queued
+        ov.submit(inputs[0][0][:-1], inputs[0][1])
+    assert torch.equal(ov.submit(*inputs[0]).wait().view(torch.int16), refs[0])
 
 
 @pytest.mark.parametrize("name,mode", [("ffn_small", "bf16"), ("ffn_small", "q8rows"),
