@@ -680,6 +680,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB copy used to scale rocprofv3 byte counters")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
               "are not part of this build (use --gpus 1).", file=sys.stderr)

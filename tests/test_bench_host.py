@@ -25,6 +25,12 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+def test_step_counts_are_checked():
+    for args in (("--steps", "0"), ("--warmup", "-1")):
+        r = _run(*args)
+        assert r.returncode == 2 and "--steps must be at least 1" in r.stderr
+
+
 def test_without_a_gpu_it_exits_with_a_message():
     import torch
     if torch.cuda.device_count() > 0:
