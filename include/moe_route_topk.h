@@ -38,8 +38,10 @@
  *  - Buffers that kernels access with 16-byte vector loads/stores must be
  *    16-byte aligned (marked "16B").
  *  - Device buffers may be reused across calls; a call overwrites everything
- *    it documents as an output.  Calls that share a buffer on different
- *    streams race.
+ *    it documents as an output.  Calls on different streams that share a
+ *    buffer race unless every one of them only reads it: inputs such as the
+ *    packed expert weights, scales, slot maps and replica maps may be shared
+ *    by calls in flight on several streams at once.
  */
 #ifndef MOE_ROUTE_TOPK_H
 #define MOE_ROUTE_TOPK_H
